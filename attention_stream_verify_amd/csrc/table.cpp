@@ -1,0 +1,202 @@
+// Segment table of a shared round: host code, no HIP calls.
+//
+// PR #1377 "LFM2: shared-round decode", shared-round commit: each layer runs
+// once over every row of every live stream from a table of the streams'
+// cache addresses, row offsets and key counts; the table carries a row map
+// and tiles, and each stream's attention partials get a range of their own.
+// The layout of every array is given in include/asv.h.
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <utility>
+#include <vector>
+
+#include "asv.h"
+
+namespace {
+
+int32_t split_keys_for(int32_t rows) {
+  const int32_t wt = rows < ASV_TILE_ROWS ? rows : ASV_TILE_ROWS;
+  if (wt <= 2) return 512;
+  if (wt <= 4) return 1024;
+  if (wt <= 8) return 2048;
+  return 4096;
+}
+
+int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// True when the byte ranges [p, p + n) overlap pairwise for no two entries.
+bool disjoint(std::vector<std::pair<uintptr_t, uintptr_t>>& spans) {
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i].first < spans[i - 1].second) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" int asv_abi_version(void) { return ASV_ABI_VERSION; }
+
+extern "C" const char* asv_strerror(int code) {
+  switch (code) {
+    case ASV_OK: return "ok";
+    case ASV_E_ARG: return "null, misaligned or aliasing pointer";
+    case ASV_E_SHAPE: return "rows, keys, capacity or layer out of range";
+    case ASV_E_UNSUPPORTED: return "dimension other than the compiled one";
+    case ASV_E_CAPACITY: return "caller buffer too small";
+    case ASV_E_HIP: return "HIP runtime refused a copy or launch";
+    default: return "unknown error code";
+  }
+}
+
+extern "C" int asv_seg_table_build(const asv_stream_desc* streams, int32_t n_streams,
+                                   const void* const* conv_state, int32_t n_conv_layers,
+                                   const void* const* k_cache, const void* const* v_cache,
+                                   int32_t n_attn_layers, void* blob, size_t blob_bytes,
+                                   asv_table_info* info) {
+  if (streams == nullptr || info == nullptr) return ASV_E_ARG;
+  if (n_streams < 1 || n_conv_layers < 0 || n_attn_layers < 0) return ASV_E_SHAPE;
+
+  // ---- descriptors
+  int64_t total_rows = 0;
+  for (int32_t s = 0; s < n_streams; ++s) {
+    const asv_stream_desc& d = streams[s];
+    if (d.rows < 1 || d.key_count < d.rows || d.key_count > ASV_MAX_KEYS) return ASV_E_SHAPE;
+    if (d.kv_capacity < d.key_count || d.kv_capacity > ASV_MAX_KEYS ||
+        d.kv_capacity % ASV_KEY_BLOCK != 0)
+      return ASV_E_SHAPE;
+    total_rows += d.rows;
+    if (total_rows > ASV_MAX_ROWS) return ASV_E_SHAPE;
+  }
+  const int32_t S = n_streams;
+  const int32_t R = static_cast<int32_t>(total_rows);
+
+  // ---- addresses: present, aligned, and no two streams sharing bytes
+  if (n_conv_layers > 0 && conv_state == nullptr) return ASV_E_ARG;
+  if (n_attn_layers > 0 && (k_cache == nullptr || v_cache == nullptr)) return ASV_E_ARG;
+  const uintptr_t state_bytes = 2u * ASV_HIDDEN * sizeof(uint16_t);
+  std::vector<std::pair<uintptr_t, uintptr_t>> spans;
+  for (int32_t l = 0; l < n_conv_layers; ++l) {
+    spans.clear();
+    for (int32_t s = 0; s < S; ++s) {
+      const void* p = conv_state[int64_t(l) * S + s];
+      if (p == nullptr || !aligned16(p)) return ASV_E_ARG;
+      const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+      spans.emplace_back(a, a + state_bytes);
+    }
+    if (!disjoint(spans)) return ASV_E_ARG;
+  }
+  for (int32_t l = 0; l < n_attn_layers; ++l) {
+    spans.clear();
+    for (int32_t s = 0; s < S; ++s) {
+      const uintptr_t bytes =
+          uintptr_t(ASV_KV_HEADS) * uintptr_t(streams[s].kv_capacity) * ASV_HEAD_DIM * sizeof(uint16_t);
+      for (const void* const* arr : {k_cache, v_cache}) {
+        const void* p = arr[int64_t(l) * S + s];
+        if (p == nullptr || !aligned16(p)) return ASV_E_ARG;
+        const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+        spans.emplace_back(a, a + bytes);
+      }
+    }
+    if (!disjoint(spans)) return ASV_E_ARG;
+  }
+
+  // ---- segments, rows, tiles, split plan, partial ranges
+  std::vector<asv_seg> segs(S);
+  std::vector<asv_row> rows(R);
+  std::vector<asv_tile> tiles;
+  int64_t poff = 0;
+  int32_t row0 = 0;
+  int32_t max_tile_rows = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    const asv_stream_desc& d = streams[s];
+    asv_seg& g = segs[s];
+    g.row0 = row0;
+    g.rows = d.rows;
+    g.keys = d.key_count;
+    g.cap = d.kv_capacity;
+    g.split_keys = split_keys_for(d.rows);
+    g.nsplit = (d.key_count + g.split_keys - 1) / g.split_keys;
+    g.poff = poff;
+    poff += int64_t(g.nsplit) * d.rows * ASV_Q_HEADS;
+    for (int32_t p = 0; p < d.rows; p += ASV_TILE_ROWS) {
+      asv_tile t;
+      t.stream = s;
+      t.row0 = row0 + p;
+      t.nrows = std::min(ASV_TILE_ROWS, d.rows - p);
+      t.pos0 = p;
+      max_tile_rows = std::max(max_tile_rows, t.nrows);
+      for (int32_t i = 0; i < t.nrows; ++i) {
+        asv_row& r = rows[t.row0 + i];
+        r.stream = s;
+        r.pos = p + i;
+        r.nkeys = d.key_count - d.rows + p + i + 1;
+        r.tile = static_cast<int32_t>(tiles.size());
+      }
+      tiles.push_back(t);
+    }
+    row0 += d.rows;
+  }
+
+  // ---- attention work: (tile, kv head, split) for every split holding a key
+  // the tile's last row sees; most keys first so long items start early.
+  std::vector<asv_work> work;
+  for (int32_t ti = 0; ti < static_cast<int32_t>(tiles.size()); ++ti) {
+    const asv_tile& t = tiles[ti];
+    const asv_seg& g = segs[t.stream];
+    const int32_t n_last = g.keys - g.rows + t.pos0 + t.nrows;
+    for (int32_t sp = 0; int64_t(sp) * g.split_keys < n_last; ++sp) {
+      const int32_t k0 = sp * g.split_keys;
+      const int32_t k1 = std::min(k0 + g.split_keys, n_last);
+      for (int32_t h = 0; h < ASV_KV_HEADS; ++h) work.push_back({ti, h, sp, k1 - k0});
+    }
+  }
+  std::stable_sort(work.begin(), work.end(),
+                   [](const asv_work& a, const asv_work& b) { return a.keys > b.keys; });
+
+  // ---- blob layout
+  asv_table_info in;
+  std::memset(&in, 0, sizeof(in));
+  in.abi_version = ASV_ABI_VERSION;
+  in.n_streams = S;
+  in.n_rows = R;
+  in.n_tiles = static_cast<int32_t>(tiles.size());
+  in.n_work = static_cast<int32_t>(work.size());
+  in.n_conv_layers = n_conv_layers;
+  in.n_attn_layers = n_attn_layers;
+  in.max_tile_rows = max_tile_rows;
+  in.partial_count = poff;
+  int64_t off = 0;
+  in.off_segs = off;       off = align16(off + int64_t(sizeof(asv_seg)) * S);
+  in.off_rows = off;       off = align16(off + int64_t(sizeof(asv_row)) * R);
+  in.off_tiles = off;      off = align16(off + int64_t(sizeof(asv_tile)) * in.n_tiles);
+  in.off_work = off;       off = align16(off + int64_t(sizeof(asv_work)) * in.n_work);
+  in.off_conv_state = off; off = align16(off + 8 * int64_t(n_conv_layers) * S);
+  in.off_k = off;          off = align16(off + 8 * int64_t(n_attn_layers) * S);
+  in.off_v = off;          off = align16(off + 8 * int64_t(n_attn_layers) * S);
+  in.blob_bytes = off;
+  *info = in;
+
+  if (blob == nullptr) return ASV_OK;
+  if (blob_bytes < static_cast<size_t>(in.blob_bytes)) return ASV_E_CAPACITY;
+
+  char* b = static_cast<char*>(blob);
+  std::memset(b, 0, static_cast<size_t>(in.blob_bytes));
+  std::memcpy(b + in.off_segs, segs.data(), sizeof(asv_seg) * S);
+  std::memcpy(b + in.off_rows, rows.data(), sizeof(asv_row) * R);
+  std::memcpy(b + in.off_tiles, tiles.data(), sizeof(asv_tile) * tiles.size());
+  if (!work.empty()) std::memcpy(b + in.off_work, work.data(), sizeof(asv_work) * work.size());
+  uint64_t* cs = reinterpret_cast<uint64_t*>(b + in.off_conv_state);
+  for (int64_t i = 0; i < int64_t(n_conv_layers) * S; ++i)
+    cs[i] = reinterpret_cast<uintptr_t>(conv_state[i]);
+  uint64_t* kp = reinterpret_cast<uint64_t*>(b + in.off_k);
+  uint64_t* vp = reinterpret_cast<uint64_t*>(b + in.off_v);
+  for (int64_t i = 0; i < int64_t(n_attn_layers) * S; ++i) {
+    kp[i] = reinterpret_cast<uintptr_t>(k_cache[i]);
+    vp[i] = reinterpret_cast<uintptr_t>(v_cache[i]);
+  }
+  return ASV_OK;
+}

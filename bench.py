@@ -1,0 +1,207 @@
+"""Benchmark of one shared verify round on one MI355X.
+
+A step is one whole round over a synthetic workload already resident in HBM:
+the table upload, 30 gated short-conv layers, 10 attention layers (split-K
+attention + merge) and the argmax over 128,000-wide logits, every layer on
+its own buffers. Default workload: long context, 4 streams x 16 window rows
+(64 rows) with 65,536 / 98,304 / 130,816 / 131,072 keys.
+
+Prints one JSON line: verify rows/s per round; the roofline of the attention
+kernel (algorithmic K/V + Q bytes per launch over its average launch time,
+timed with HIP events on the stream it runs on, against 8 TB/s); and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD_NAMES = {
+    0: "tiny: 4 streams, windows 1-4, keys 16-256",
+    1: "decode: 16 streams x 1 row, keys 512-4096",
+    2: "draft verify: 16 streams x 8 rows, keys 2k-32k",
+    3: "long context: 4 streams x 16 rows, keys 65,536-131,072",
+    4: "full scratch: 2,048 rows, 48 windows + prompt chunks, lognormal keys",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=3, choices=[0, 1, 2, 3, 4])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--seed", type=int, default=None)
+    return p.parse_args()
+
+
+def layer_order(n_conv, n_attn):
+    """Interleave the layers as the model does: every fourth layer attends."""
+    order, c, a = [], 0, 0
+    while c < n_conv or a < n_attn:
+        if a < n_attn and (len(order) % 4 == 3 or c >= n_conv):
+            order.append(("attn", a))
+            a += 1
+        else:
+            order.append(("conv", c))
+            c += 1
+    return order
+
+
+def cpu_baseline(rnd, R):
+    """The oracle, as it stands, on one conv layer, one attention layer and the
+    argmax of this workload, scaled to a round by 30 / 10 / 1."""
+    import numpy as np
+
+    import workloads
+    from oracle import argmax as oargmax
+    from oracle import attn as oattn
+    from oracle import conv as oconv
+    from oracle import table as otable
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+
+    def u16(t):
+        return t.detach().cpu().numpy().view(np.uint16)
+
+    X, W, states = rnd.conv[0]
+    Q, ks, vs = rnd.attn[0]
+    Xh, Wh, sth = u16(X), u16(W), [u16(s) for s in states]
+    Qh, Kh = u16(Q), [u16(k) for k in ks]
+    Vh = [u16(workloads.v_logical(v)) for v in vs]
+    Lh = u16(rnd.logits)
+    t = otable.build(rnd.streams)
+    t0 = time.perf_counter()
+    oconv.shared_conv(t, Xh, Wh, sth)
+    t1 = time.perf_counter()
+    po, pm, pl, _ = oattn.partials(t, Qh, Kh, Vh)
+    oattn.merge(t, po, pm, pl)
+    t2 = time.perf_counter()
+    oargmax.row_argmax(Lh)
+    t3 = time.perf_counter()
+    t_round = rnd.n_conv * (t1 - t0) + rnd.n_attn * (t2 - t1) + (t3 - t2)
+    return {
+        "value": R / t_round, "unit": "rows/s", "cores": int(cores), "kind": "oracle",
+        "sample": (f"one conv layer ({t1 - t0:.2f} s), one attention layer with partials "
+                   f"and merge ({t2 - t1:.2f} s) and the argmax ({t3 - t2:.2f} s) over all "
+                   f"{R} rows of this workload, scaled by {rnd.n_conv}/{rnd.n_attn}/1 "
+                   f"to a {t_round:.1f} s round"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_stream_verify_amd as asv
+    import workloads
+
+    asv.lib()  # fails loudly when libasv.so is missing
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    rnd = workloads.Round(args.config, device=dev, seed=args.seed)
+    R, S = rnd.R, rnd.S
+    rb = asv.RoundBuffers(rnd.streams, [layer[2] for layer in rnd.conv],
+                          [layer[1] for layer in rnd.attn], [layer[2] for layer in rnd.attn],
+                          device=dev, vocab=rnd.logits.shape[1])
+    order = layer_order(rnd.n_conv, rnd.n_attn)
+    sum_keys = sum(k for _, k, _ in rnd.streams)
+    attn_bytes = 2048 * sum_keys + 4096 * R            # K/V once + Q, per launch
+    merge_bytes = 4096 * R                              # O written (partials are a means)
+
+    def step(ev=None):
+        rb.upload()
+        for kind, i in order:
+            if kind == "conv":
+                X, W, _ = rnd.conv[i]
+                rb.conv(i, X, W)
+            else:
+                if ev is not None:
+                    ev.append(torch.cuda.Event(enable_timing=True))
+                    ev[-1].record()
+                rb.attn(i, rnd.attn[i][0])
+                if ev is not None:
+                    ev.append(torch.cuda.Event(enable_timing=True))
+                    ev[-1].record()
+                rb.merge()
+        rb.argmax(rnd.logits)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    attn_ev = []
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step(attn_ev)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    attn_ms = [attn_ev[i].elapsed_time(attn_ev[i + 1]) for i in range(0, len(attn_ev), 2)]
+    attn_avg_ms = sum(attn_ms) / len(attn_ms)
+    achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+
+    line = {
+        "metric": "verify rows/sec per shared round (conv+attn+argmax); attn HBM GB/s vs peak",
+        "value": R / (ms_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[args.config],
+            "streams": S,
+            "rows": R,
+            "sum_keys": sum_keys,
+            "conv_layers": rnd.n_conv,
+            "attn_layers": rnd.n_attn,
+            "vocab": int(rnd.logits.shape[1]),
+            "seed": rnd.seed,
+        },
+        "roofline": {
+            "kernel": "attn_split (asv_shared_attn)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_launch": attn_bytes,
+            "avg_launch_us": attn_avg_ms * 1e3,
+        },
+        "attn_merge_bytes_per_layer": attn_bytes + merge_bytes,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(rnd, R)
+        line["cpu_baseline"]["gpu_over_cpu"] = line["value"] / line["cpu_baseline"]["value"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -19,7 +19,8 @@ sees every key. The pages print no formula; the readings here are:
   (-inf, 0, 0);
 * the merge takes M = max_t m_t and returns
   sum_t exp(m_t - M) l_t o_t / sum_t exp(m_t - M) l_t over the row's splits
-  in split order, skipping empty ones.
+  in split order, skipping empty ones (l = 0); a NaN in any partial makes
+  the output NaN.
 
 K and V are given per stream in their logical layout [8][keys][64] (bf16 bit
 patterns); only the first K_s keys are read.
@@ -111,10 +112,10 @@ def merge(table, o, m, l, rows=None):
         nt = table.row_nsplit(r)
         for h in range(N_Q_HEADS):
             recs = [table.record(r, h, t) for t in range(nt)]
-            recs = [x for x in recs if l[x] > 0.0]
+            recs = [x for x in recs if l[x] != 0.0]      # empty splits only
             if not recs:
                 continue
-            M = max(m[x] for x in recs)
+            M = np.max(m[recs])                          # NaN propagates
             num = np.zeros(HEAD_DIM, dtype=np.float64)
             den = 0.0
             for x in recs:

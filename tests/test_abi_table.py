@@ -1,0 +1,164 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host table builder is bit-exact against the oracle's independent builder
+(no GPU call is made here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
+
+import workloads
+from oracle import table as otable
+
+asv = pytest.importorskip("attention_stream_verify_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "asv.h")).read()
+    return sorted(set(re.findall(r"\b(asv_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_what_the_binding_knows():
+    assert _declared() == sorted(asv.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(asv._lib.LIB_PATH)
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert asv.abi_version() == 1
+    assert asv.strerror(-4) == "caller buffer too small"
+
+
+def _fake_ptrs(streams, n_layers, nbytes_fn, base):
+    """Distinct, 16-byte aligned, non-overlapping fake addresses (never dereferenced)."""
+    out, addr = [], base
+    for _ in range(n_layers):
+        layer = []
+        for s in streams:
+            layer.append(addr)
+            addr += ((nbytes_fn(s) + 4095) // 4096) * 4096
+        out.append(layer)
+    return out
+
+
+def _build(streams, n_conv=1, n_attn=1):
+    cs = _fake_ptrs(streams, n_conv, lambda s: 8192, 1 << 40)
+    kp = _fake_ptrs(streams, n_attn, lambda s: 8 * s[2] * 64 * 2, 1 << 42)
+    vp = _fake_ptrs(streams, n_attn, lambda s: 8 * s[2] * 64 * 2, 1 << 44)
+    info, blob = asv.seg_table_build(streams, cs, kp, vp)
+    return info, blob, asv.table_arrays(info, blob), (cs, kp, vp)
+
+
+def _compare(streams):
+    info, blob, t, (cs, kp, vp) = _build(streams)
+    o = otable.build(streams)
+    S, R = len(streams), o.n_rows
+    assert (info.n_streams, info.n_rows, info.n_tiles) == (S, R, len(o.tiles))
+    assert info.partial_count == o.partial_count
+    segs = t["segs"]
+    assert np.array_equal(segs["row0"], o.seg_off[:-1])
+    assert np.array_equal(segs["rows"], o.rows) and np.array_equal(segs["keys"], o.keys)
+    assert np.array_equal(segs["cap"], o.caps)
+    assert np.array_equal(segs["split_keys"], o.split)
+    assert np.array_equal(segs["nsplit"], o.nsplit)
+    assert np.array_equal(segs["poff"], o.poff)
+    rows = t["rows"]
+    assert np.array_equal(rows["stream"], o.row_stream)
+    assert np.array_equal(rows["pos"], o.row_pos)
+    assert np.array_equal(rows["nkeys"], o.row_nkeys)
+    tiles = np.stack([t["tiles"][f] for f in ("stream", "row0", "nrows", "pos0")], axis=1)
+    assert np.array_equal(tiles, o.tiles)
+    for r in range(R):
+        tt = o.tiles[rows["tile"][r]]
+        assert tt[1] <= r < tt[1] + tt[2]
+    # work items: the same set (their order is a schedule), keys = visited keys
+    w = t["work"]
+    got = sorted(zip(w["tile"].tolist(), w["head"].tolist(), w["split"].tolist()))
+    assert got == sorted(map(tuple, o.work.tolist()))
+    assert all(w["keys"][i] >= w["keys"][i + 1] for i in range(len(w) - 1))
+    for ti, h, sp, k in zip(w["tile"], w["head"], w["split"], w["keys"]):
+        s, _r0, n, p0 = o.tiles[ti]
+        last = o.keys[s] - o.rows[s] + p0 + n
+        assert k == min((sp + 1) * o.split[s], last) - sp * o.split[s] > 0
+    assert np.array_equal(t["conv_state"], np.array(cs, dtype=np.uint64).ravel())
+    assert np.array_equal(t["k"], np.array(kp, dtype=np.uint64).ravel())
+    assert np.array_equal(t["v"], np.array(vp, dtype=np.uint64).ravel())
+
+
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+def test_table_bit_exact_on_workloads(config):
+    _compare(workloads.streams_for(config))
+
+
+_stream = st.integers(1, 600).flatmap(
+    lambda w: st.integers(w, 131072).map(lambda k: (w, k, min(((k + 31) // 32) * 32 + 32 * (k % 3), 131072))))
+
+
+@settings(max_examples=80, deadline=None)
+@given(st.lists(_stream, min_size=1, max_size=12).filter(lambda s: sum(w for w, _, _ in s) <= 2048))
+def test_table_bit_exact_random(streams):
+    _compare(streams)
+
+
+def test_size_query_and_capacity():
+    streams = workloads.streams_for(0)
+    info, blob, _, (cs, kp, vp) = _build(streams)
+    small = np.zeros(int(info.blob_bytes) - 16, dtype=np.uint8)
+    with pytest.raises(asv.AsvError) as e:
+        asv.seg_table_build(streams, cs, kp, vp, blob=small)
+    assert e.value.code == -4
+    assert not small.any()  # nothing written on failure
+
+
+@pytest.mark.parametrize("streams,code", [
+    ([(0, 16, 32)], -2), ([(4, 3, 32)], -2), ([(1, 131073, 131104)], -2), ([(1, 64, 32)], -2),
+    ([(1, 16, 48)], -2), ([(1, 16, 131104)], -2), ([(16, 32, 32)] * 129, -2),
+])
+def test_refusals_match_the_oracle(streams, code):
+    with pytest.raises(ValueError):
+        otable.build(streams)
+    with pytest.raises(asv.AsvError) as e:
+        _build(streams)
+    assert e.value.code == code
+
+
+def test_refuses_aliasing_and_misaligned_addresses():
+    streams = [(1, 100, 128), (2, 100, 128)]
+    _, _, _, (cs, kp, vp) = _build(streams)
+    # every stream reading the first stream's conv state / kv cache
+    for bad in ([[cs[0][0], cs[0][0]]], None):
+        if bad is None:
+            break
+        with pytest.raises(asv.AsvError) as e:
+            asv.seg_table_build(streams, bad, kp, vp)
+        assert e.value.code == -1
+    with pytest.raises(asv.AsvError) as e:
+        asv.seg_table_build(streams, cs, [[kp[0][0], kp[0][0]]], vp)
+    assert e.value.code == -1
+    with pytest.raises(asv.AsvError) as e:
+        asv.seg_table_build(streams, cs, kp, [[vp[0][0], vp[0][0] + 64]])
+    assert e.value.code == -1
+    with pytest.raises(asv.AsvError) as e:      # a K cache overlapping another stream's V
+        asv.seg_table_build(streams, cs, [[kp[0][0], vp[0][0]]], vp)
+    assert e.value.code == -1
+    with pytest.raises(asv.AsvError) as e:
+        asv.seg_table_build(streams, [[cs[0][0] + 8, cs[0][1]]], kp, vp)
+    assert e.value.code == -1
+    with pytest.raises(asv.AsvError) as e:
+        asv.seg_table_build(streams, [[0, cs[0][1]]], kp, vp)
+    assert e.value.code == -1
+
+
+def test_tables_without_layers_and_counts_at_1_32_2048_rows():
+    for streams, expect in [([(1, 4096, 4096)], 256), ([(1, 1000, 1024)] * 32, 2048),
+                            ([(16, 131072, 131072)] * 128, 128 * 16 * 32 * 32)]:
+        info, _ = asv.seg_table_build(streams)
+        assert info.n_rows in (1, 32, 2048) and info.partial_count == expect
+        assert info.partial_count == otable.build(streams).partial_count

@@ -174,3 +174,26 @@ def test_shared_round_rows_equal_each_stream_alone():
         ta = table.build([st_])
         alone = attn.attention(ta, Q[r0:r1], [K[s]], [V[s]])
         assert np.array_equal(alone, full[r0:r1])
+
+
+def test_merge_skips_empty_splits_and_propagates_nan():
+    streams = [(1, 2000, 2048)]                      # 4 splits of 512
+    t, Q, K, V = _round(streams, 8)
+    po, pm, pl, _ = attn.partials(t, Q, K, V)
+    base = attn.merge(t, po, pm, pl)
+    # an empty split (m = -inf, l = 0, o = 0) changes nothing: drop split 1 of
+    # head 0 from the reference by hand and compare with the merge of the rest
+    recs = [t.record(0, 0, sp) for sp in range(4)]
+    keep = [recs[0], recs[2], recs[3]]
+    M = max(pm[x] for x in keep)
+    wts = np.array([np.exp(pm[x] - M) * pl[x] for x in keep])
+    by_hand = (wts[:, None] * po[keep]).sum(axis=0) / wts.sum()
+    pm2, pl2, po2 = pm.copy(), pl.copy(), po.copy()
+    pm2[recs[1]], pl2[recs[1]], po2[recs[1]] = -np.inf, 0.0, 0.0
+    out = attn.merge(t, po2, pm2, pl2)
+    assert np.allclose(out[0, 0], by_hand, atol=1e-14)
+    assert np.array_equal(out[0, 1:], base[0, 1:])
+    # a NaN partial is not an empty one: it reaches the output
+    pl3 = pl.copy()
+    pl3[recs[2]] = np.nan
+    assert np.isnan(attn.merge(t, po, pm, pl3)[0, 0]).all()

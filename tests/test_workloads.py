@@ -56,3 +56,13 @@ def test_tiny_logits_plants():
         if flag[r]:
             continue
         assert pick[r] == min(hi, lo)
+
+
+def test_logit_plants_on_every_workload_small_vocab():
+    g = torch.Generator().manual_seed(5)
+    for config, R in [(0, 10), (1, 16), (2, 128), (3, 64), (4, 2048)]:
+        L, notes = workloads.logits_for(config, R, g, "cpu", vocab=1000)
+        assert L.shape == (R, 1000)
+        pick, flag = argmax.row_argmax(L.numpy().view(np.uint16))
+        expect_flags = {0: 1, 1: 0, 2: 2, 3: 0, 4: 8}[config]
+        assert int(flag.sum()) == expect_flags

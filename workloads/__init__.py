@@ -181,7 +181,7 @@ def logits_for(config, R, g, device, vocab=VOCAB):
                 b = int(rng.integers(0, a))
             else:
                 continue
-            L[r, b] = L[r, a]
+            L[r, b] = L[r, a].clone()
             notes.append(("tie", r, a, b))
         pos = int(rng.integers(0, vocab))
         L[nan_row, pos] = NAN
@@ -192,7 +192,7 @@ def logits_for(config, R, g, device, vocab=VOCAB):
         for r in rows:
             a = row_max_pos(r)
             pos = torch.from_numpy(rng.choice(vocab, size=nt, replace=False)).to(device)
-            L[r, pos] = L[r, a]
+            L[r, pos] = L[r, a].clone()
             notes.append(("ties", r, nt))
         if config == 4:
             bad = rng.choice(R, size=8, replace=False)
