@@ -7,21 +7,25 @@
 // bx = bf16(B*x), three causal taps over [state, bx...], gate C, and the
 // state advanced to the last two steps.
 //
-// Mapping: a block covers 4 rows of one 16-row tile and all 2,048 channels;
-// each of its 256 threads owns 8 channels (16-byte loads of B, C, x: one
-// block reads 4 KB contiguous per input third). Rows are independent once
-// bx of the two rows before them is known, so a block recomputes those from
-// X instead of waiting for another block. Only the block holding a stream's
-// first rows touches the stream's state: it reads the state, then writes the
-// new one, so no other thread ever reads a state that is being rewritten.
+// Mapping: a 64-thread block covers 2 rows of one 16-row tile and 512 of the
+// 2,048 channels; each thread owns 8 channels (16-byte loads of B, C, x: one
+// block reads 1 KB contiguous per input third). Small rounds are latency
+// bound, so the grid is made wide (tiles x 8 row pairs x 4 channel groups)
+// rather than deep. Rows are independent once bx of the two rows before them
+// is known, so a block recomputes those from X instead of waiting for
+// another block. Only the blocks holding a stream's first two rows (the only
+// rows that read the state) touch the stream's state: each reads its
+// channels of the state, then writes them anew, so no thread ever reads a
+// state that another thread is rewriting.
 
 #include "device.h"
 
 namespace asv {
 namespace {
 
-constexpr int kThreads = 256;   // 8 channels each -> 2,048
-constexpr int kRowsPerBlock = 4;
+constexpr int kThreads = 64;    // 8 channels each -> 512 a block
+constexpr int kChannelGroups = ASV_HIDDEN / (kThreads * 8);
+constexpr int kRowsPerBlock = 2;
 constexpr int kSub = ASV_TILE_ROWS / kRowsPerBlock;
 
 // bx for 8 channels of one row: bf16(B * x), exact product in fp32.
@@ -46,13 +50,13 @@ __global__ __launch_bounds__(kThreads) void conv_rows(TableView tv, int layer,
                                                       const uint16_t* __restrict__ X,
                                                       const uint16_t* __restrict__ W,
                                                       uint16_t* __restrict__ Y) {
-  const asv_tile T = tv.tiles[blockIdx.x];
+  const asv_tile T = gload(tv.tiles + blockIdx.x);
   const int i0 = blockIdx.y * kRowsPerBlock;
   if (i0 >= T.nrows) return;
   const int i1 = min(i0 + kRowsPerBlock, T.nrows);
-  const asv_seg S = tv.segs[T.stream];
+  const asv_seg S = gload(tv.segs + T.stream);
   const int p0 = T.pos0 + i0;           // window position of the block's first row
-  const int c0 = threadIdx.x * 8;
+  const int c0 = (blockIdx.z * kThreads + threadIdx.x) * 8;
 
   // taps of 8 channels: W[c][0..2] for c = c0..c0+7, 48 contiguous bytes
   float w0[8], w1[8], w2[8];
@@ -75,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void conv_rows(TableView tv, int layer,
   }
 
   uint16_t* state = reinterpret_cast<uint16_t*>(
-      tv.conv_state[int64_t(layer) * tv.n_streams + T.stream]);
+      gload(tv.conv_state + int64_t(layer) * tv.n_streams + T.stream));
   float h0[8], h1[8];
   if (p0 == 0) {
     const u32x4 s0 = load16(state + c0);
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void conv_rows(TableView tv, int layer,
       h1[2 * k + 1] = bf16_hi(s1[k]);
     }
   } else {
-    // p0 >= 4: the two history steps before the block are bx of rows p0-2, p0-1
+    // p0 >= 2: the two history steps before the block are bx of rows p0-2, p0-1
     bx8(X + int64_t(S.row0 + p0 - 2) * ASV_CONV_IN, c0, h0);
     bx8(X + int64_t(S.row0 + p0 - 1) * ASV_CONV_IN, c0, h1);
   }
@@ -135,7 +139,8 @@ extern "C" int asv_shared_conv(const asv_table_info* info, const void* dev_blob,
     return ASV_E_ARG;
   if (layer < 0 || layer >= info->n_conv_layers) return ASV_E_SHAPE;
   const asv::TableView tv = asv::make_view(*info, dev_blob);
-  hipLaunchKernelGGL(asv::conv_rows, dim3(unsigned(info->n_tiles), asv::kSub), dim3(asv::kThreads),
+  hipLaunchKernelGGL(asv::conv_rows, dim3(unsigned(info->n_tiles), asv::kSub, asv::kChannelGroups),
+                     dim3(asv::kThreads),
                      0, static_cast<hipStream_t>(stream), tv, int(layer), x, w, y);
   return hipGetLastError() == hipSuccess ? ASV_OK : ASV_E_HIP;
 }

@@ -29,11 +29,95 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+// Global-memory (address space 1) accesses. Pointers read out of the table
+// are generic to the compiler; without the cast their loads become FLAT
+// loads, which also count against the LDS wait counter, so every LDS or
+// cross-lane wait would drain every load in flight.
+#define ASV_GLOBAL __attribute__((address_space(1)))
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+  return *(const ASV_GLOBAL u32x4*)(p);
 }
 
-__device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void store16(void* p, u32x4 v) { *(ASV_GLOBAL u32x4*)(p) = v; }
+
+__device__ __forceinline__ void store16f(float* p, f32x4 v) { *(ASV_GLOBAL f32x4*)(p) = v; }
+
+// Typed global load/store. Class types (table records, float2) move as raw
+// words and are bit-cast, since address-space-qualified class copies are not
+// expressible; every such type here is 8 bytes or a multiple of 16.
+template <typename T>
+__device__ __forceinline__ T gload(const T* p) {
+  if constexpr (!__is_class(T)) {
+    return *(const ASV_GLOBAL T*)(p);
+  } else if constexpr (sizeof(T) == 8) {
+    return __builtin_bit_cast(T, *(const ASV_GLOBAL unsigned long long*)(p));
+  } else {
+    static_assert(sizeof(T) % 16 == 0, "record size");
+    struct Words {
+      u32x4 w[sizeof(T) / 16];
+    } v;
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(T) / 16; ++i) v.w[i] = ((const ASV_GLOBAL u32x4*)(p))[i];
+    return __builtin_bit_cast(T, v);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void gstore(T* p, T v) {
+  if constexpr (!__is_class(T)) {
+    *(ASV_GLOBAL T*)(p) = v;
+  } else {
+    static_assert(sizeof(T) == 8, "record size");
+    *(ASV_GLOBAL unsigned long long*)(p) = __builtin_bit_cast(unsigned long long, v);
+  }
+}
+
+// Table records read by every lane are the same for the whole wave; moving
+// their fields to scalar registers lets the compiler branch on them with
+// scalar branches instead of exec masks.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ asv_tile uniform(asv_tile r) {
+  return asv_tile{uni(r.stream), uni(r.row0), uni(r.nrows), uni(r.pos0)};
+}
+__device__ __forceinline__ asv_work uniform(asv_work r) {
+  return asv_work{uni(r.tile), uni(r.head), uni(r.split), uni(r.keys)};
+}
+__device__ __forceinline__ asv_row uniform(asv_row r) {
+  return asv_row{uni(r.stream), uni(r.pos), uni(r.nkeys), uni(r.tile)};
+}
+__device__ __forceinline__ asv_seg uniform(asv_seg r) {
+  const uint64_t p = uint64_t(r.poff);
+  const int64_t poff = int64_t((uint64_t(uint32_t(uni(int(uint32_t(p >> 32))))) << 32) |
+                               uint64_t(uint32_t(uni(int(uint32_t(p))))));
+  return asv_seg{uni(r.row0), uni(r.rows), uni(r.keys), uni(r.cap), uni(r.split_keys),
+                 uni(r.nsplit), poff};
+}
+
+__device__ __forceinline__ uint64_t uniform_ptr(uint64_t p) {
+  return (uint64_t(uint32_t(uni(int(uint32_t(p >> 32))))) << 32) | uint64_t(uint32_t(uni(int(uint32_t(p)))));
+}
+
+// Butterflies across the 16-lane rows of a wave64 on the VALU (gfx950
+// v_permlane16_swap / v_permlane32_swap): every lane gets op(x[l], x[l ^ 16])
+// or op(x[l], x[l ^ 32]). No LDS traffic and no LDS wait.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // The table as the kernels see it: the uploaded blob plus the offsets that
 // asv_seg_table_build reported.

@@ -39,7 +39,24 @@ def parse():
     p.add_argument("--config", type=int, default=3, choices=[0, 1, 2, 3, 4])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB three times (the known-size "
+                        "kernel that scales HBM byte counters) and exit")
     return p.parse_args()
+
+
+def calibrate_copy(mib):
+    """A plain copy of a known size: its FETCH_SIZE / WRITE_SIZE counters give
+    the factor between those counters and the bytes a kernel really moves."""
+    import torch
+    n = mib << 20
+    src = torch.randint(0, 127, (n,), dtype=torch.int8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "reads": n, "writes": n}), flush=True)
 
 
 def layer_order(n_conv, n_attn):
@@ -106,6 +123,10 @@ def main():
         print(f"bench.py runs on one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
 
