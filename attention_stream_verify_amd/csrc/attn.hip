@@ -81,6 +81,11 @@ constexpr int kStageKeys = 128;
 constexpr int kSubBytes = 8192;
 constexpr int kStageBytes = 4 * kSubBytes;
 
+#ifndef ASV_ATTN_REG_STAGES
+#define ASV_ATTN_REG_STAGES 2
+#endif
+constexpr int kRegStages = ASV_ATTN_REG_STAGES;  // stages in flight in registers
+
 struct StageRegs {
   u32x4 k[4], v[4];
 };
@@ -280,27 +285,25 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
     vofs = 4096 + ((d >> 4) * 64 + swz((t & 3) * 16 + (d & 15), 0)) * 16;
   }
 
-  // stages in flight: two in registers while one is consumed from LDS; two
-  // LDS slots, one barrier a stage (a slot is rewritten only after every
-  // wave has passed the barrier that follows its last read)
+  // stages in flight: kRegStages in registers while one is consumed from
+  // LDS; two LDS slots, one barrier a stage (a slot is rewritten only after
+  // every wave has passed the barrier that follows its last read)
   const int nst = (k1 - k0 + kStageKeys - 1) / kStageKeys;
-  char* slot0 = lds;
-  char* slot1 = lds + kStageBytes;
-  StageRegs r0, r1;
-  stage_load(r0, Kh, Vh, k0, last_sb, t);
-  stage_load(r1, Kh, Vh, k0 + min(1, nst - 1) * kStageKeys, last_sb, t);
-  // Both halves of an iteration always store, prefetch (clamped) and pass
-  // the barrier, so every iteration leaves the same loads in flight and the
-  // wait before a store covers only that stage; an odd last stage just
-  // skips its compute.
-  for (int i = 0; i < nst; i += 2) {
+  StageRegs r[kRegStages];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kRegStages; ++h)
+    stage_load(r[h], Kh, Vh, k0 + min(h, nst - 1) * kStageKeys, last_sb, t);
+  // Every step of an iteration stores, prefetches (clamped) and passes the
+  // barrier, so every iteration leaves the same loads in flight and the wait
+  // before a store covers only that stage; steps past the last stage skip
+  // their compute.
+  for (int i = 0; i < nst; i += kRegStages) {
+#pragma unroll
+    for (int h = 0; h < kRegStages; ++h) {
       const int si = i + h;
-      StageRegs& r = h ? r1 : r0;
-      char* slot = h ? slot1 : slot0;
-      stage_store(r, slot, kofs, vofs);
-      stage_load(r, Kh, Vh, k0 + min(si + 2, nst - 1) * kStageKeys, last_sb, t);
+      char* slot = lds + (si & 1) * kStageBytes;
+      stage_store(r[h], slot, kofs, vofs);
+      stage_load(r[h], Kh, Vh, k0 + min(si + kRegStages, nst - 1) * kStageKeys, last_sb, t);
       __syncthreads();
       const int ks = k0 + si * kStageKeys;
       if (!active || si >= nst) continue;

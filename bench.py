@@ -59,6 +59,35 @@ def calibrate_copy(mib):
     print(json.dumps({"calibrate_copy_bytes": n, "reads": n, "writes": n}), flush=True)
 
 
+TRAFFIC_PROFILES = {3: "profiles/attn_split_long_context_traffic.md"}
+
+
+def profiled_traffic(config):
+    """HBM bytes a launch of the attention kernel moved under rocprofv3
+    (FETCH_SIZE and WRITE_SIZE passes, scaled by a plain-copy calibration),
+    as recorded in profiles/ -- or None when there is no profile for this
+    workload or the kernel sources changed since it was taken."""
+    import hashlib
+    name = TRAFFIC_PROFILES.get(config)
+    if name is None or not os.path.exists(os.path.join(ROOT, name)):
+        return None
+    fields = {}
+    for line in open(os.path.join(ROOT, name)):
+        if ":" in line and line.split(":", 1)[0].strip() in (
+                "traffic_bytes_per_launch", "kernel_sources_sha256", "kernel_sources"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if len(fields) != 3:
+        return None
+    h = hashlib.sha256()
+    for src in fields["kernel_sources"].split():
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != fields["kernel_sources_sha256"]:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def layer_order(n_conv, n_attn):
     """Interleave the layers as the model does: every fourth layer attends."""
     order, c, a = [], 0, 0
@@ -211,7 +240,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": profiled_traffic(args.config),
             "bytes_per_launch": attn_bytes,
             "avg_launch_us": attn_avg_ms * 1e3,
         },
