@@ -98,8 +98,8 @@ __device__ __forceinline__ void stage_load(StageRegs& r, const uint16_t* __restr
     // sub-blocks past the split's last one re-read that one (a cache hit):
     // every stage issues the same loads, so waits stay exact
     const int sb = min(ks + 32 * j, last_sb);
-    r.k[j] = load16(Kh + int64_t(sb + (t >> 3)) * ASV_HEAD_DIM + (t & 7) * 8);
-    r.v[j] = load16(Vh + int64_t(sb >> 5) * (ASV_HEAD_DIM * 32) + t * 8);
+    r.k[j] = load16_stream(Kh + int64_t(sb + (t >> 3)) * ASV_HEAD_DIM + (t & 7) * 8);
+    r.v[j] = load16_stream(Vh + int64_t(sb >> 5) * (ASV_HEAD_DIM * 32) + t * 8);
   }
 }
 
@@ -227,8 +227,8 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int G = lane >> 4;
   const int c16 = lane & 15;
-  const asv_tile T = uniform(gload(tv.tiles + wk.tile));
-  const asv_seg S = uniform(gload(tv.segs + T.stream));
+  const asv_tile T = uniform(cload(tv.tiles + wk.tile));
+  const asv_seg S = uniform(cload(tv.segs + T.stream));
   const int g = wk.head;
   // q groups: 1 (one q tile), 2 (two), 4 (three or four; a fourth group
   // with no rows only helps load)
@@ -243,8 +243,8 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
   const int last_sb = ((k1 - 1) >> 5) << 5;
   const int64_t head_elems = int64_t(S.cap) * ASV_HEAD_DIM;
   const int64_t sel = int64_t(layer) * tv.n_streams + T.stream;
-  const uint16_t* Kh = reinterpret_cast<const uint16_t*>(uniform_ptr(gload(tv.kp + sel))) + g * head_elems;
-  const uint16_t* Vh = reinterpret_cast<const uint16_t*>(uniform_ptr(gload(tv.vp + sel))) + g * head_elems;
+  const uint16_t* Kh = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.kp + sel))) + g * head_elems;
+  const uint16_t* Vh = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.vp + sel))) + g * head_elems;
 
   // Q operands (B of the score MFMA) and each column's visible key count
   WaveState<QPW> st;
@@ -380,8 +380,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split(TableView tv, int laye
                                                           float* __restrict__ pml) {
   // two stage slots (64 KB); the fold area after the loop reuses them
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
-  const asv_work wk = uniform(gload(tv.work + blockIdx.x));
-  const int nqt = (uni(gload(tv.tiles + wk.tile).nrows) + 3) >> 2;
+  const asv_work wk = uniform(cload(tv.work + blockIdx.x));
+  const int nqt = (uni(cload(tv.tiles + wk.tile).nrows) + 3) >> 2;
   attn_item<QPW_MAX>(tv, layer, Q, po, pml, wk, nqt, lds);
 }
 
@@ -408,8 +408,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_rows(TableView tv,
   const int lane = threadIdx.x & 63;
   const int r = pair / ASV_Q_HEADS;
   const int h = pair - r * ASV_Q_HEADS;
-  const asv_row row = gload(tv.rows + r);
-  const asv_seg S = gload(tv.segs + row.stream);
+  const asv_row row = uniform(cload(tv.rows + r));
+  const asv_seg S = uniform(cload(tv.segs + row.stream));
   const int nt = (row.nkeys + S.split_keys - 1) / S.split_keys;
   const int64_t rec0 = S.poff + int64_t(row.pos) * ASV_Q_HEADS + h;
   const int64_t step = int64_t(S.rows) * ASV_Q_HEADS;

@@ -39,6 +39,12 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *(const ASV_GLOBAL u32x4*)(p);
 }
 
+// Read-once streams (K/V caches): non-temporal, so they do not push other
+// data out of the caches.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load((const ASV_GLOBAL u32x4*)(p));
+}
+
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *(ASV_GLOBAL u32x4*)(p) = v; }
 
 __device__ __forceinline__ void store16f(float* p, f32x4 v) { *(ASV_GLOBAL f32x4*)(p) = v; }
@@ -59,6 +65,28 @@ __device__ __forceinline__ T gload(const T* p) {
     } v;
 #pragma unroll
     for (unsigned i = 0; i < sizeof(T) / 16; ++i) v.w[i] = ((const ASV_GLOBAL u32x4*)(p))[i];
+    return __builtin_bit_cast(T, v);
+  }
+}
+
+// Table reads at a wave-uniform address: through the constant address space
+// (the table does not change during a launch) they become scalar loads into
+// SGPRs, with the scalar cache's shorter latency, instead of vector loads.
+#define ASV_CONST __attribute__((address_space(4)))
+
+template <typename T>
+__device__ __forceinline__ T cload(const T* p) {
+  if constexpr (!__is_class(T)) {
+    return *(const ASV_CONST T*)(p);
+  } else if constexpr (sizeof(T) == 8) {
+    return __builtin_bit_cast(T, *(const ASV_CONST unsigned long long*)(p));
+  } else {
+    static_assert(sizeof(T) % 16 == 0, "record size");
+    struct Words {
+      u32x4 w[sizeof(T) / 16];
+    } v;
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(T) / 16; ++i) v.w[i] = ((const ASV_CONST u32x4*)(p))[i];
     return __builtin_bit_cast(T, v);
   }
 }
