@@ -8,21 +8,21 @@
 //
 // Work item = (16-row tile, kv head, split), one 256-thread block each. A
 // tile's q vectors are its rows x the 4 q heads of the kv head (up to 64),
-// in column tiles of 16. The block's 4 waves load each 128-key stage of K
-// and V together into an LDS ring (two stages in flight in registers) and
-// then split the work: 16-row tiles give each wave one q tile over every
-// key; smaller tiles split the keys between waves, which fold their states
-// through LDS in a fixed order at the end.
+// in column tiles of 16. Every wave of the block holds all of the tile's q
+// tiles and streams its own quarter of the split's keys (32-key sub-blocks
+// w, w+4, ...) through a private LDS ring that direct global->LDS loads
+// fill; at the end the four waves fold their states through LDS in wave
+// order. Tiles of 13-16 rows keep their Q operands in LDS, read per q tile,
+// so that the four q tiles' accumulators fit in registers.
 //
 // Per 32-key sub-block, on the bf16 16x16x32 MFMA (fp32 accumulate):
 //   S^T[key][q]  = K[key][:] . Q[q][:]        (2 key tiles x 2 d-steps)
 //   O^T[d][q]   += V^T[d][key] P^T[key][q]    (4 d tiles, P split hi + lo)
-// K rows are key-major in HBM, V is d-major inside 32-key blocks, and the
-// LDS ring holds both in MFMA operand order, so each operand is one
-// conflict-free 16-byte LDS read.
+// K rows are key-major in HBM, V is d-major inside 32-key blocks; each
+// operand is one conflict-free 16-byte LDS read.
 //
 // Lane l (G = l/16, c = l%16) of a score tile holds keys 8G+i (first tile)
-// and 8G+4+i (second tile), i = 0..3, for q column c: the stage's K rows are
+// and 8G+4+i (second tile), i = 0..3, for q column c: the K rows are
 // placed so that these 8 keys are exactly the ones the lane supplies as the
 // P operand of the PV MFMA, whose V operand is V^T[d][8G..8G+7]. P is fed
 // as two bf16 parts (hi = the top 16 bits of the fp32 weight, lo = the
@@ -69,72 +69,102 @@ struct WaveState {
 
 constexpr float kLazy = 8.0f;
 
-// A stage is 128 keys of one kv head: four 32-key sub-blocks, each K 4 KB +
-// V 4 KB. The block's 256 threads load a stage together (thread t: 16 bytes
-// of K and 16 of V of every sub-block, each wave reading 1 KB contiguous)
-// two stages ahead, and store it into an LDS slot in MFMA operand order:
-// inside a sub-block, K operand (tile X, d-step s) of lane l sits at
-// ((2X + s)*64 + l)*16 bytes and V operand (d tile dt) of lane l at
-// 4096 + (dt*64 + l)*16, so each operand read is a conflict-free
-// ds_read_b128 at lane*16.
-constexpr int kStageKeys = 128;
+// Each wave streams its own 32-key sub-blocks (the item's sub-blocks w,
+// w+4, w+8, ... for wave w) through a private two-slot LDS ring filled by
+// direct global->LDS loads (global_load_lds_dwordx4): no registers hold data
+// in flight and no block barrier paces the waves. A load instruction puts
+// lane l's 16 bytes at (its 1 KB group) + l*16, and every instruction reads
+// one whole 1 KB run of HBM (lanes may take its 16-byte chunks in any order
+// at full speed; instructions that cover half-lines of 16 rows run ~15%
+// slower). Group j of K holds key rows 8j..8j+7 with the chunks permuted so
+// that the score MFMA's operand reads hit 16 distinct 16-byte bank groups
+// per 16 lanes (k_fetch / k_read below); group 4+dt of V holds V^T rows
+// 16dt..16dt+15, which is already one 1 KB run in the d-major V layout:
+// lane (G, c) fetches the operand it reads back, V^T[16dt + c][8G..8G+7].
+// 8 KB a slot.
 constexpr int kSubBytes = 8192;
-constexpr int kStageBytes = 4 * kSubBytes;
 
-#ifndef ASV_ATTN_REG_STAGES
-#define ASV_ATTN_REG_STAGES 2
-#endif
-constexpr int kRegStages = ASV_ATTN_REG_STAGES;  // stages in flight in registers
-
-struct StageRegs {
-  u32x4 k[4], v[4];
-};
-
-__device__ __forceinline__ void stage_load(StageRegs& r, const uint16_t* __restrict__ Kh,
-                                           const uint16_t* __restrict__ Vh, int ks, int last_sb,
-                                           int t) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // sub-blocks past the split's last one re-read that one (a cache hit):
-    // every stage issues the same loads, so waits stay exact
-    const int sb = min(ks + 32 * j, last_sb);
-    r.k[j] = load16_stream(Kh + int64_t(sb + (t >> 3)) * ASV_HEAD_DIM + (t & 7) * 8);
-    r.v[j] = load16_stream(Vh + int64_t(sb >> 5) * (ASV_HEAD_DIM * 32) + t * 8);
-  }
+// Score-MFMA lane (G, c) supplies, for key tile X and d-step s, key row
+// 8(c>>2) + 4X + (c&3), d-columns 8(4s+G)..+7: row 4X + (c&3) of K group
+// j = c>>2. k_fetch gives the byte offset, inside group j (key rows
+// 8j..8j+7, 128 B each), of the 16-byte chunk lane l fetches; bits of l:
+// b5 = X, b4 = G>>1, b3 = (G&1)^(j>>1), b2 = s^(j&1), b1b0 = (c&3)^G.
+__device__ __forceinline__ uint32_t k_fetch(int l, int j) {
+  const int G = (((l >> 4) & 1) << 1) | (((l >> 3) & 1) ^ ((j >> 1) & 1));
+  const int s = ((l >> 2) & 1) ^ (j & 1);
+  const int r = 4 * ((l >> 5) & 1) + ((l & 3) ^ G);
+  return uint32_t(r * 128 + (4 * s + G) * 16);
 }
 
-// Operand slot of lane l inside a 64-lane group, XOR-swizzled within its
-// 16-lane block (lane c of block G goes to c ^ 2G ^ x). Readers stay a
-// permutation of 256 contiguous bytes per 16 lanes (conflict-free); a
-// store pass (one K row's 8 chunks, or 2 d-rows x 4 key groups of V) now
-// spreads over all 8 16-byte slots of a 128-byte bank row.
-__device__ __forceinline__ int swz(int l, int x) { return (l & 48) | ((l & 15) ^ ((l >> 3) & 6) ^ x); }
-
-__device__ __forceinline__ void stage_store(const StageRegs& r, char* slot, int kofs, int vofs) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    *reinterpret_cast<u32x4*>(slot + j * kSubBytes + kofs) = r.k[j];
-    *reinterpret_cast<u32x4*>(slot + j * kSubBytes + vofs) = r.v[j];
-  }
+// LDS byte offset (within a slot) of the K operand of score-MFMA lane
+// (G, c) for key tile X = 0 and d-step s; key tile 1 is 512 bytes on.
+__device__ __forceinline__ uint32_t k_read(int G, int c, int s) {
+  const int j = c >> 2;
+  const int l = ((G >> 1) << 4) | (((G & 1) ^ (j >> 1)) << 3) | ((s ^ (j & 1)) << 2) | ((c & 3) ^ G);
+  return uint32_t(j * 1024 + l * 16);
 }
 
-// One 32-key sub-block for QPW q tiles; operands come from LDS.
+// 16 bytes from (wave-uniform base + per-lane byte offset) to LDS at
+// l + lane*16. The offset is passed through an opaque register copy so the
+// compiler keeps it a 32-bit register next to a scalar base (the
+// scalar-base form of global_load_lds_dwordx4) instead of hoisting a 64-bit
+// per-lane address for every load out of the loop.
+// AUX is the load's cache policy: kStream (non-temporal) for K/V that one
+// work item alone reads, 0 where several tiles of a stream re-read it.
+template <int AUX>
+__device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, void* l) {
+  uint32_t o;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(o) : "v"(off));
+  const ASV_GLOBAL char* b = (const ASV_GLOBAL char*)(base);
+  __builtin_amdgcn_global_load_lds((const ASV_GLOBAL void*)(b + o),
+                                   (__attribute__((address_space(3))) void*)(l), 16, 0, AUX);
+}
+
+constexpr int kStream = 2;  // the nt bit of the cache-policy operand
+
+// Wait until at most n vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int AUX>
+__device__ __forceinline__ void issue_sub(char* slot, const uint16_t* __restrict__ Kh,
+                                          const uint16_t* __restrict__ Vh, int kb,
+                                          const uint32_t (&koff)[4], uint32_t voff) {
+  const char* kbase = reinterpret_cast<const char*>(Kh + int64_t(kb) * ASV_HEAD_DIM);
+  const char* vbase = reinterpret_cast<const char*>(Vh + int64_t(kb >> 5) * (ASV_HEAD_DIM * 32));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lds_dma16<AUX>(kbase, koff[j], slot + j * 1024);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) lds_dma16<AUX>(vbase + dt * 1024, voff, slot + 4096 + dt * 1024);
+}
+
+// Wide tiles keep their Q operands in LDS (read per q tile) rather than in
+// 32 registers, which a wave holding four q tiles cannot spare.
+template <int QPW>
+constexpr bool q_in_lds() { return QPW >= 4; }
+
+// One 32-key sub-block for QPW q tiles; K/V operands come from the wave's
+// slot, Q operands from registers or (wide tiles) from the block's Q area.
 template <int QPW>
 __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, int n_first,
-                                          const u32x4 (&qop)[QPW][2], const int (&nq)[QPW],
-                                          WaveState<QPW>& st, int lane) {
+                                          const u32x4 (&qop)[QPW][2], const char* qlds,
+                                          const int (&nq)[QPW], WaveState<QPW>& st, int lane,
+                                          uint32_t kr0, uint32_t kr1) {
   const int G = lane >> 4;
   const float c = kScale * kLog2e;
   const float lazy_raw = kLazy / c;
   const float ninf = -__builtin_inff();
-  const int l0 = swz(lane, 0), l1 = swz(lane, 1);
-  const u32x4 ka0 = *reinterpret_cast<const u32x4*>(sub + (0 * 64 + l0) * 16);
-  const u32x4 ka1 = *reinterpret_cast<const u32x4*>(sub + (1 * 64 + l1) * 16);
-  const u32x4 kb0 = *reinterpret_cast<const u32x4*>(sub + (2 * 64 + l0) * 16);
-  const u32x4 kb1 = *reinterpret_cast<const u32x4*>(sub + (3 * 64 + l1) * 16);
+  auto rd = [&](uint32_t off) { return *reinterpret_cast<const u32x4*>(sub + off); };
+  const u32x4 ka0 = rd(kr0);
+  const u32x4 ka1 = rd(kr1);
+  const u32x4 kb0 = rd(kr0 + 512);
+  const u32x4 kb1 = rd(kr1 + 512);
   u32x4 v[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) v[dt] = *reinterpret_cast<const u32x4*>(sub + 4096 + (dt * 64 + l0) * 16);
+  for (int dt = 0; dt < 4; ++dt) v[dt] = rd(4096 + dt * 1024 + lane * 16);
   if (kb + 32 > keys) {  // slots past the key count may hold anything
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -144,10 +174,18 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, int
   const bool edge = kb + 32 > n_first;
 #pragma unroll
   for (int u = 0; u < QPW; ++u) {
-    f32x4 sa = mfma(ka0, qop[u][0], f32x4{0.f, 0.f, 0.f, 0.f});
-    sa = mfma(ka1, qop[u][1], sa);
-    f32x4 sb = mfma(kb0, qop[u][0], f32x4{0.f, 0.f, 0.f, 0.f});
-    sb = mfma(kb1, qop[u][1], sb);
+    u32x4 q0, q1;
+    if constexpr (q_in_lds<QPW>()) {
+      q0 = *reinterpret_cast<const u32x4*>(qlds + (2 * u) * 1024 + lane * 16);
+      q1 = *reinterpret_cast<const u32x4*>(qlds + (2 * u + 1) * 1024 + lane * 16);
+    } else {
+      q0 = qop[u][0];
+      q1 = qop[u][1];
+    }
+    f32x4 sa = mfma(ka0, q0, f32x4{0.f, 0.f, 0.f, 0.f});
+    sa = mfma(ka1, q1, sa);
+    f32x4 sb = mfma(kb0, q0, f32x4{0.f, 0.f, 0.f, 0.f});
+    sb = mfma(kb1, q1, sb);
     float sc[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
     if (edge) {
 #pragma unroll
@@ -187,6 +225,8 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, int
       st.acc[dt][u] = mfma(v[dt], hi, st.acc[dt][u]);
       st.acc[dt][u] = mfma(v[dt], lo, st.acc[dt][u]);
     }
+    // keep one q tile's temporaries live at a time (four tiles would spill)
+    if constexpr (QPW >= 4) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -212,58 +252,76 @@ __device__ __forceinline__ void fold(WaveState<QPW>& a, float mref_b, float mtru
   }
 }
 
-// A block of 4 waves runs one work item. The waves load every stage
-// together; for computing they split the item's q tiles into QG groups of
-// QPW tiles and each stage's four sub-blocks into KG = 4/QG interleaved
-// groups (wave (qg, kg) takes sub-blocks kg, kg+KG, ...). A q group's waves
-// fold their states through LDS in key-group order at the end.
-template <int QPW>
+// A block of 4 waves runs one work item; every wave holds all QPW q tiles
+// of the tile (QPW = ceil(rows/4)) and its own stripe of the split's keys;
+// at the end the waves fold their states through LDS in wave order.
+template <int QPW, int AUX>
 __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
                                           const uint16_t* __restrict__ Q, float* __restrict__ po,
-                                          float* __restrict__ pml, const asv_work wk, int nqt,
-                                          char* __restrict__ lds) {
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+                                          float* __restrict__ pml, const asv_work wk,
+                                          char* __restrict__ ringA, char* __restrict__ ringB,
+                                          char* __restrict__ qlds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = lane >> 4;
   const int c16 = lane & 15;
   const asv_tile T = uniform(cload(tv.tiles + wk.tile));
   const asv_seg S = uniform(cload(tv.segs + T.stream));
   const int g = wk.head;
-  // q groups: 1 (one q tile), 2 (two), 4 (three or four; a fourth group
-  // with no rows only helps load)
-  const int QG = (nqt >= 3) ? 4 : nqt;
-  const int KG = kWaves / QG;
-  const int qg = wave / KG;
-  const int kg = wave - qg * KG;
   const int base_n = S.keys - S.rows + T.pos0;  // tile row i sees base_n + i + 1 keys
   const int n_first = base_n + 1;
   const int k0 = wk.split * S.split_keys;
   const int k1 = min(k0 + S.split_keys, base_n + T.nrows);
-  const int last_sb = ((k1 - 1) >> 5) << 5;
   const int64_t head_elems = int64_t(S.cap) * ASV_HEAD_DIM;
   const int64_t sel = int64_t(layer) * tv.n_streams + T.stream;
   const uint16_t* Kh = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.kp + sel))) + g * head_elems;
   const uint16_t* Vh = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.vp + sel))) + g * head_elems;
 
-  // Q operands (B of the score MFMA) and each column's visible key count
+  // per-lane byte offsets: HBM chunks fetched into K group j and V group dt
+  // (1 KB on per dt), and the K operands read back for d-steps 0 and 1
+  uint32_t koff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) koff[j] = uint32_t(j * 1024) + k_fetch(lane, j);
+  const uint32_t voff = uint32_t(c16 * 64 + G * 16);  // V^T[16dt + c16][8G .. 8G+7]
+  const uint32_t kr0 = k_read(G, c16, 0), kr1 = k_read(G, c16, 1);
+
+  // Q operands (B of the score MFMA) and each column's visible key count.
+  // Wide tiles: wave w fetches q tile w into the block's Q area in operand
+  // order (tile u, d-step s at (2u + s)*1 KB + lane*16); the barrier after
+  // the ring's first fill publishes it.
   WaveState<QPW> st;
   u32x4 qop[QPW][2];
   int nq[QPW];
   const float ninf = -__builtin_inff();
+  auto q_ptr = [&](int u) -> const uint16_t* {
+    const int q = u * 16 + c16;
+    return Q + (int64_t(T.row0 + (q >> 2)) * ASV_Q_HEADS + g * 4 + (q & 3)) * ASV_HEAD_DIM + 8 * G;
+  };
+  if constexpr (q_in_lds<QPW>()) {
+    const int u = wave;
+    u32x4 a = u32x4{0u, 0u, 0u, 0u}, b = u32x4{0u, 0u, 0u, 0u};
+    if (((u * 16 + c16) >> 2) < T.nrows) {
+      a = load16(q_ptr(u));
+      b = load16(q_ptr(u) + 32);
+    }
+    *reinterpret_cast<u32x4*>(qlds + (2 * u) * 1024 + lane * 16) = a;
+    *reinterpret_cast<u32x4*>(qlds + (2 * u + 1) * 1024 + lane * 16) = b;
+  }
 #pragma unroll
   for (int u = 0; u < QPW; ++u) {
-    const int q = (qg * QPW + u) * 16 + c16;
+    const int q = u * 16 + c16;
     const int rt = q >> 2;
     if (rt < T.nrows) {
-      const uint16_t* qp =
-          Q + (int64_t(T.row0 + rt) * ASV_Q_HEADS + g * 4 + (q & 3)) * ASV_HEAD_DIM + 8 * G;
-      qop[u][0] = load16(qp);
-      qop[u][1] = load16(qp + 32);
+      if constexpr (!q_in_lds<QPW>()) {
+        qop[u][0] = load16(q_ptr(u));
+        qop[u][1] = load16(q_ptr(u) + 32);
+      }
       nq[u] = base_n + rt + 1;
     } else {
-      qop[u][0] = u32x4{0u, 0u, 0u, 0u};
-      qop[u][1] = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (!q_in_lds<QPW>()) {
+        qop[u][0] = u32x4{0u, 0u, 0u, 0u};
+        qop[u][1] = u32x4{0u, 0u, 0u, 0u};
+      }
       nq[u] = 0;
     }
     st.mref[u] = ninf;
@@ -273,56 +331,50 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
     for (int dt = 0; dt < 4; ++dt) st.acc[dt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const bool active = qg * QPW * 16 < T.nrows * 4;  // the group holds a real q column
+  char* slotA = ringA + wave * kSubBytes;
+  char* slotB = ringB + wave * kSubBytes;
+  const int stride = kWaves * 32;
+  const int first = k0 + wave * 32;
+  const int nb = first < k1 ? (k1 - first + stride - 1) / stride : 0;
 
-  // where this thread's 16-byte pieces of a sub-block go in operand order
-  int kofs, vofs;
-  {
-    const int kk = t >> 3, ch = t & 7;  // K: key kk, 16-byte chunk ch of its row
-    const int X = (kk >> 2) & 1, m = ((kk >> 3) << 2) | (kk & 3), sd = ch >> 2;
-    kofs = ((2 * X + sd) * 64 + swz((ch & 3) * 16 + m, sd)) * 16;
-    const int d = t >> 2;               // V: dim d, keys 8*(t&3) .. +7
-    vofs = 4096 + ((d >> 4) * 64 + swz((t & 3) * 16 + (d & 15), 0)) * 16;
+  // first ring fill after the Q loads, then retire the Q loads: the loop's
+  // waits then count ring loads only
+  if (nb > 0) {
+    issue_sub<AUX>(slotA, Kh, Vh, first, koff, voff);
+    wait_vm<8>();
+  } else {
+    wait_vm<0>();
   }
+  if constexpr (q_in_lds<QPW>()) __syncthreads();  // the Q area is written
 
-  // stages in flight: kRegStages in registers while one is consumed from
-  // LDS; two LDS slots, one barrier a stage (a slot is rewritten only after
-  // every wave has passed the barrier that follows its last read)
-  const int nst = (k1 - k0 + kStageKeys - 1) / kStageKeys;
-  StageRegs r[kRegStages];
-#pragma unroll
-  for (int h = 0; h < kRegStages; ++h)
-    stage_load(r[h], Kh, Vh, k0 + min(h, nst - 1) * kStageKeys, last_sb, t);
-  // Every step of an iteration stores, prefetches (clamped) and passes the
-  // barrier, so every iteration leaves the same loads in flight and the wait
-  // before a store covers only that stage; steps past the last stage skip
-  // their compute.
-  for (int i = 0; i < nst; i += kRegStages) {
-#pragma unroll
-    for (int h = 0; h < kRegStages; ++h) {
-      const int si = i + h;
-      char* slot = lds + (si & 1) * kStageBytes;
-      stage_store(r[h], slot, kofs, vofs);
-      stage_load(r[h], Kh, Vh, k0 + min(si + kRegStages, nst - 1) * kStageKeys, last_sb, t);
-      __syncthreads();
-      const int ks = k0 + si * kStageKeys;
-      if (!active || si >= nst) continue;
-      for (int sbi = kg; sbi < 4; sbi += KG) {
-        const int kb = ks + 32 * sbi;
-        if (kb >= k1) break;
-        sub_block<QPW>(slot + sbi * kSubBytes, kb, S.keys, n_first, qop, nq, st, lane);
-      }
+  // two-slot ring: while one slot is consumed the next sub-block's 8 loads
+  // are in flight
+  for (int i = 0; i < nb; i += 2) {
+    if (i + 1 < nb) {
+      issue_sub<AUX>(slotB, Kh, Vh, first + (i + 1) * stride, koff, voff);
+      wait_vm<8>();
+    } else {
+      wait_vm<0>();
     }
+    sub_block<QPW>(slotA, first + i * stride, S.keys, n_first, qop, qlds, nq, st, lane, kr0, kr1);
+    if (i + 1 >= nb) break;
+    if (i + 2 < nb) {
+      issue_sub<AUX>(slotA, Kh, Vh, first + (i + 2) * stride, koff, voff);
+      wait_vm<8>();
+    } else {
+      wait_vm<0>();
+    }
+    sub_block<QPW>(slotB, first + (i + 1) * stride, S.keys, n_first, qop, qlds, nq, st, lane, kr0, kr1);
   }
 #pragma unroll
   for (int u = 0; u < QPW; ++u) st.l[u] = add_xor32(add_xor16(st.l[u]));
-  __syncthreads();  // the ring is reused for the fold
+  __syncthreads();  // the rings are reused for the fold
 
-  // fold the key groups of each q group in order through LDS
-  float* fl = reinterpret_cast<float*>(lds);
+  // fold the waves' states in wave order through LDS
+  float* fl = reinterpret_cast<float*>(ringA);
   constexpr int kSlot = QPW * 64 * 19;  // mref, mtrue, l, then 4 x QPW f32x4 per lane
-  if (kg > 0) {
-    float* my = fl + (qg * (kWaves - 1) + kg - 1) * kSlot;
+  if (wave > 0) {
+    float* my = fl + (wave - 1) * kSlot;
 #pragma unroll
     for (int u = 0; u < QPW; ++u) {
       my[u * 64 + lane] = st.mref[u];
@@ -334,9 +386,9 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
     }
   }
   __syncthreads();
-  if (kg != 0) return;
-  for (int w = 1; w < KG; ++w) {
-    const float* o = fl + (qg * (kWaves - 1) + w - 1) * kSlot;
+  if (wave != 0) return;
+  for (int w = 1; w < kWaves; ++w) {
+    const float* o = fl + (w - 1) * kSlot;
 #pragma unroll
     for (int u = 0; u < QPW; ++u) {
       f32x4 accb[4];
@@ -352,7 +404,7 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
   const float c = kScale * kLog2e;
 #pragma unroll
   for (int u = 0; u < QPW; ++u) {
-    const int q = (qg * QPW + u) * 16 + c16;
+    const int q = u * 16 + c16;
     const int rt = q >> 2;
     if (rt >= T.nrows) continue;
     const int64_t rec =
@@ -378,11 +430,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split(TableView tv, int laye
                                                           const uint16_t* __restrict__ Q,
                                                           float* __restrict__ po,
                                                           float* __restrict__ pml) {
-  // two stage slots (64 KB); the fold area after the loop reuses them
-  __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
+  // two ring slots per wave, as two arrays so the compiler can tell a slot
+  // being loaded from the one being read; the fold reuses them afterwards
+  __shared__ __attribute__((aligned(16))) char ringA[kWaves * kSubBytes];
+  __shared__ __attribute__((aligned(16))) char ringB[kWaves * kSubBytes];
+  __shared__ __attribute__((aligned(16))) char qarea[QPW_MAX >= 4 ? 8 * 1024 : 16];
   const asv_work wk = uniform(cload(tv.work + blockIdx.x));
-  const int nqt = (uni(cload(tv.tiles + wk.tile).nrows) + 3) >> 2;
-  attn_item<QPW_MAX>(tv, layer, Q, po, pml, wk, nqt, lds);
+  const asv_tile T = uniform(cload(tv.tiles + wk.tile));
+  const int nqt = (T.nrows + 3) >> 2;
+  // a stream of one tile reads its K/V in exactly one item: stream it past
+  // the caches; tiles of a longer stream re-read the same keys
+  const bool once = uni(cload(tv.segs + T.stream).rows) <= ASV_TILE_ROWS;
+  if constexpr (QPW_MAX >= 4) {
+    if (nqt == 4) {
+      if (once) return attn_item<4, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
+      return attn_item<4, 0>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
+    }
+  }
+  if constexpr (QPW_MAX >= 3) {
+    if (nqt == 3) {
+      if (once) return attn_item<3, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
+      return attn_item<3, 0>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
+    }
+  }
+  if constexpr (QPW_MAX >= 2) {
+    if (nqt == 2) {
+      if (once) return attn_item<2, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
+      return attn_item<2, 0>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
+    }
+  }
+  if (once) return attn_item<1, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
+  attn_item<1, 0>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
 }
 
 // Merge: one wave per (row, q head); lane d owns output dim d. The wave
@@ -456,7 +534,12 @@ extern "C" int asv_shared_attn(const asv_table_info* info, const void* dev_blob,
   float* pml = partials + info->partial_count * ASV_HEAD_DIM;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(unsigned(info->n_work)), block(asv::kThreads);
-  hipLaunchKernelGGL(asv::attn_split<1>, grid, block, 0, st, tv, int(layer), q, po, pml);
+  switch ((info->max_tile_rows + 3) >> 2) {
+    case 1: hipLaunchKernelGGL(asv::attn_split<1>, grid, block, 0, st, tv, int(layer), q, po, pml); break;
+    case 2: hipLaunchKernelGGL(asv::attn_split<2>, grid, block, 0, st, tv, int(layer), q, po, pml); break;
+    case 3: hipLaunchKernelGGL(asv::attn_split<3>, grid, block, 0, st, tv, int(layer), q, po, pml); break;
+    default: hipLaunchKernelGGL(asv::attn_split<4>, grid, block, 0, st, tv, int(layer), q, po, pml); break;
+  }
   return hipGetLastError() == hipSuccess ? ASV_OK : ASV_E_HIP;
 }
 
