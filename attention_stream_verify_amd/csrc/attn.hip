@@ -56,18 +56,25 @@ __device__ __forceinline__ uint32_t zero_past(uint32_t w, int key, int keys) {
   return w;
 }
 
-// Per-wave online-softmax state for QPW q tiles. The wave keeps, per q
-// column, a reference max mref (the exponent base) and the true running max
-// mtrue. mref moves only when a block's max exceeds it by more than kLazy in
-// log2 units, so the accumulators are rescaled rarely (weights stay below
-// 2^kLazy); at the end l is brought to the true max, which a record holds.
+// Per-wave online-softmax state for QPW q tiles. Per q column the wave
+// keeps an exponent base mref (raw score units; -inf until the column has
+// seen a key) and nmc = -mref*c, the sum l of its weights at that base, and
+// pm, the bits of the largest weight so far (weights are >= 0, so their
+// bits order as unsigned integers). A sub-block's weights are computed at
+// the current base straight away; only when one of them exceeds 2^kLazy
+// (a score more than kLazy/c above the base) does the wave take the rebase
+// path, which moves the base to the column max and rescales. So the common
+// path has no max reduction at all, and the accumulators are rescaled
+// rarely. At the end the true max follows from the largest weight:
+// mtrue = mref + log2(pm)/c, and l at the true max is l / pm.
 template <int QPW>
 struct WaveState {
   f32x4 acc[4][QPW];
-  float mref[QPW], mtrue[QPW], l[QPW];
+  float mref[QPW], nmc[QPW], mtrue[QPW], l[QPW];
+  uint32_t pm[QPW];
 };
 
-constexpr float kLazy = 8.0f;
+constexpr uint32_t kLazyBits = 0x43800000u;  // 256.0f: weights stay <= 2^8
 
 // Each wave streams its own 32-key sub-blocks (the item's sub-blocks w,
 // w+4, w+8, ... for wave w) through a private two-slot LDS ring filled by
@@ -110,14 +117,16 @@ __device__ __forceinline__ uint32_t k_read(int G, int c, int s) {
 // scalar-base form of global_load_lds_dwordx4) instead of hoisting a 64-bit
 // per-lane address for every load out of the loop.
 // AUX is the load's cache policy: kStream (non-temporal) for K/V that one
-// work item alone reads, 0 where several tiles of a stream re-read it.
-template <int AUX>
+// work item alone reads, 0 where several tiles of a stream re-read it. IMM
+// is the instruction's immediate offset, which moves the global and the LDS
+// address alike.
+template <int AUX, int IMM = 0>
 __device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, void* l) {
   uint32_t o;
   asm volatile("v_mov_b32 %0, %1" : "=v"(o) : "v"(off));
   const ASV_GLOBAL char* b = (const ASV_GLOBAL char*)(base);
   __builtin_amdgcn_global_load_lds((const ASV_GLOBAL void*)(b + o),
-                                   (__attribute__((address_space(3))) void*)(l), 16, 0, AUX);
+                                   (__attribute__((address_space(3))) void*)(l), 16, IMM, AUX);
 }
 
 constexpr int kStream = 2;  // the nt bit of the cache-policy operand
@@ -137,8 +146,10 @@ __device__ __forceinline__ void issue_sub(char* slot, const uint16_t* __restrict
   const char* vbase = reinterpret_cast<const char*>(Vh + int64_t(kb >> 5) * (ASV_HEAD_DIM * 32));
 #pragma unroll
   for (int j = 0; j < 4; ++j) lds_dma16<AUX>(kbase, koff[j], slot + j * 1024);
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) lds_dma16<AUX>(vbase + dt * 1024, voff, slot + 4096 + dt * 1024);
+  lds_dma16<AUX, 0>(vbase, voff, slot + 4096);
+  lds_dma16<AUX, 1024>(vbase, voff, slot + 4096);
+  lds_dma16<AUX, 2048>(vbase, voff, slot + 4096);
+  lds_dma16<AUX, 3072>(vbase, voff, slot + 4096);
 }
 
 // Wide tiles keep their Q operands in LDS (read per q tile) rather than in
@@ -146,18 +157,91 @@ __device__ __forceinline__ void issue_sub(char* slot, const uint16_t* __restrict
 template <int QPW>
 constexpr bool q_in_lds() { return QPW >= 4; }
 
+__device__ __forceinline__ uint32_t umax3(uint32_t a, uint32_t b, uint32_t c) {
+  return a > b ? (a > c ? a : c) : (b > c ? b : c);
+}
+
+// Weights of one q tile's 8 scores at base -nmc/c, and the bits of the largest.
+__device__ __forceinline__ uint32_t weights(const float (&sc)[8], float nmc, float (&p)[8]) {
+  const float c = kScale * kLog2e;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) p[jj] = exp2_(__builtin_fmaf(sc[jj], c, nmc));
+  const uint32_t m0 = umax3(__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]));
+  const uint32_t m1 = umax3(__float_as_uint(p[3]), __float_as_uint(p[4]), __float_as_uint(p[5]));
+  return umax3(m0, m1, umax3(__float_as_uint(p[6]), __float_as_uint(p[7]), 0u));
+}
+
+// Does any weight of these 8 scores exceed 2^kLazy at base -nmc/c?
+__device__ __forceinline__ bool weights_over(const float (&sc)[8], float nmc) {
+  float p[8];
+  return weights(sc, nmc, p) > kLazyBits;
+}
+
+// Rebase q tile u (wave-uniform, rare): every column moves its base up to
+// its max so far; x * 1.0f leaves the bits of columns that do not move
+// unchanged.
+template <int QPW>
+__device__ __forceinline__ void rebase(WaveState<QPW>& st, int u, const float (&sc)[8]) {
+  const float c = kScale * kLog2e;
+  const float ninf = -__builtin_inff();
+  float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                   fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  mx = max_xor32(max_xor16(mx));
+  const float mn = fmaxf(st.mref[u], mx);
+  const float alpha = (mn > st.mref[u]) ? exp2_((st.mref[u] - mn) * c) : 1.f;
+  st.mref[u] = mn;
+  st.nmc[u] = (mn == ninf) ? 0.f : -mn * c;
+  st.l[u] *= alpha;
+  st.pm[u] = __float_as_uint(__uint_as_float(st.pm[u]) * alpha);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) st.acc[dt][u] *= alpha;
+}
+
+// Weights of q tile u's 8 scores at the current base into l, pm and, as
+// bf16 hi + lo, through the PV MFMAs into the accumulators.
+template <int QPW>
+__device__ __forceinline__ void accumulate(WaveState<QPW>& st, int u, const float (&sc)[8],
+                                           const u32x4 (&v)[4]) {
+  float p[8];
+  const uint32_t pmax = weights(sc, st.nmc[u], p);
+  st.pm[u] = st.pm[u] > pmax ? st.pm[u] : pmax;
+  st.l[u] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  u32x4 hi, lo;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    // hi = top halves of two weights in one v_perm_b32; lo = what they drop
+    const uint32_t a = __float_as_uint(p[2 * w]);
+    const uint32_t b = __float_as_uint(p[2 * w + 1]);
+    hi[w] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+    const float ra = p[2 * w] - __uint_as_float(a & 0xFFFF0000u);
+    const float rb = p[2 * w + 1] - __uint_as_float(b & 0xFFFF0000u);
+    lo[w] = __builtin_amdgcn_perm(__float_as_uint(rb), __float_as_uint(ra), 0x07060302u);
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    st.acc[dt][u] = mfma(v[dt], hi, st.acc[dt][u]);
+    st.acc[dt][u] = mfma(v[dt], lo, st.acc[dt][u]);
+  }
+}
+
 // One 32-key sub-block for QPW q tiles; K/V operands come from the wave's
 // slot, Q operands from registers or (wide tiles) from the block's Q area.
-template <int QPW>
-__device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, int n_first,
+// EDGE: the sub-block reaches past some row's causal limit or past the key
+// count, so scores are masked and V past the key count is zeroed. first:
+// the wave's first sub-block, which always sets the bases.
+template <int QPW, bool EDGE>
+__device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, bool first,
                                           const u32x4 (&qop)[QPW][2], const char* qlds,
                                           const int (&nq)[QPW], WaveState<QPW>& st, int lane,
-                                          uint32_t kr0, uint32_t kr1) {
+                                          uint32_t kr0) {
   const int G = lane >> 4;
-  const float c = kScale * kLog2e;
-  const float lazy_raw = kLazy / c;
   const float ninf = -__builtin_inff();
   auto rd = [&](uint32_t off) { return *reinterpret_cast<const u32x4*>(sub + off); };
+  // d-step 1 flips bit 2 of the chunk index; computed here by an opaque
+  // instruction so that it is not hoisted into a second register that the
+  // four-q-tile loop cannot spare
+  uint32_t kr1;
+  asm volatile("v_xor_b32 %0, 64, %1" : "=v"(kr1) : "v"(kr0));
   const u32x4 ka0 = rd(kr0);
   const u32x4 ka1 = rd(kr1);
   const u32x4 kb0 = rd(kr0 + 512);
@@ -165,13 +249,14 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, int
   u32x4 v[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) v[dt] = rd(4096 + dt * 1024 + lane * 16);
-  if (kb + 32 > keys) {  // slots past the key count may hold anything
+  if constexpr (EDGE) {
+    if (kb + 32 > keys) {  // slots past the key count may hold anything
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) v[dt][w] = zero_past(v[dt][w], kb + 8 * G + 2 * w, keys);
+        for (int w = 0; w < 4; ++w) v[dt][w] = zero_past(v[dt][w], kb + 8 * G + 2 * w, keys);
+    }
   }
-  const bool edge = kb + 32 > n_first;
 #pragma unroll
   for (int u = 0; u < QPW; ++u) {
     u32x4 q0, q1;
@@ -187,43 +272,20 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, int
     f32x4 sb = mfma(kb0, q0, f32x4{0.f, 0.f, 0.f, 0.f});
     sb = mfma(kb1, q1, sb);
     float sc[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-    if (edge) {
+    if constexpr (EDGE) {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj)
         if (kb + 8 * G + jj >= nq[u]) sc[jj] = ninf;
     }
-    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    mx = max_xor32(max_xor16(mx));
-    st.mtrue[u] = fmaxf(st.mtrue[u], mx);
-    const bool move = mx > st.mref[u] + lazy_raw;
-    if (__any(move)) {  // wave-uniform; x * 1.0f leaves the other columns' bits unchanged
-      const float alpha = move ? exp2_((st.mref[u] - mx) * c) : 1.f;
-      st.mref[u] = move ? mx : st.mref[u];
-      st.l[u] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) st.acc[dt][u] *= alpha;
-    }
-    const float nmc = -((st.mref[u] == ninf) ? 0.f : st.mref[u]) * c;
-    float p[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) p[jj] = exp2_(__builtin_fmaf(sc[jj], c, nmc));
-    st.l[u] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    u32x4 hi, lo;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // hi = top halves of two weights in one v_perm_b32; lo = what they drop
-      const uint32_t a = __float_as_uint(p[2 * w]);
-      const uint32_t b = __float_as_uint(p[2 * w + 1]);
-      hi[w] = __builtin_amdgcn_perm(b, a, 0x07060302u);
-      const float ra = p[2 * w] - __uint_as_float(a & 0xFFFF0000u);
-      const float rb = p[2 * w + 1] - __uint_as_float(b & 0xFFFF0000u);
-      lo[w] = __builtin_amdgcn_perm(__float_as_uint(rb), __float_as_uint(ra), 0x07060302u);
-    }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      st.acc[dt][u] = mfma(v[dt], hi, st.acc[dt][u]);
-      st.acc[dt][u] = mfma(v[dt], lo, st.acc[dt][u]);
+    // Each path finishes the q tile itself (weights into l, pm and the PV
+    // MFMAs): were the paths to join before the accumulation, the join
+    // would cost register copies of the weights and the state on the
+    // common path.
+    if (first || __any(weights_over(sc, st.nmc[u]))) {
+      rebase<QPW>(st, u, sc);
+      accumulate<QPW>(st, u, sc, v);
+    } else {
+      accumulate<QPW>(st, u, sc, v);
     }
     // keep one q tile's temporaries live at a time (four tiles would spill)
     if constexpr (QPW >= 4) __builtin_amdgcn_sched_barrier(0);
@@ -283,7 +345,7 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
 #pragma unroll
   for (int j = 0; j < 4; ++j) koff[j] = uint32_t(j * 1024) + k_fetch(lane, j);
   const uint32_t voff = uint32_t(c16 * 64 + G * 16);  // V^T[16dt + c16][8G .. 8G+7]
-  const uint32_t kr0 = k_read(G, c16, 0), kr1 = k_read(G, c16, 1);
+  const uint32_t kr0 = k_read(G, c16, 0);
 
   // Q operands (B of the score MFMA) and each column's visible key count.
   // Wide tiles: wave w fetches q tile w into the block's Q area in operand
@@ -325,8 +387,9 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
       nq[u] = 0;
     }
     st.mref[u] = ninf;
-    st.mtrue[u] = ninf;
+    st.nmc[u] = 0.f;
     st.l[u] = 0.f;
+    st.pm[u] = 0u;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) st.acc[dt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -356,7 +419,13 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
     } else {
       wait_vm<0>();
     }
-    sub_block<QPW>(slotA, first + i * stride, S.keys, n_first, qop, qlds, nq, st, lane, kr0, kr1);
+    {
+      const int kb = first + i * stride;
+      if (kb + 32 > n_first)
+        sub_block<QPW, true>(slotA, kb, S.keys, i == 0, qop, qlds, nq, st, lane, kr0);
+      else
+        sub_block<QPW, false>(slotA, kb, S.keys, i == 0, qop, qlds, nq, st, lane, kr0);
+    }
     if (i + 1 >= nb) break;
     if (i + 2 < nb) {
       issue_sub<AUX>(slotA, Kh, Vh, first + (i + 2) * stride, koff, voff);
@@ -364,10 +433,24 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
     } else {
       wait_vm<0>();
     }
-    sub_block<QPW>(slotB, first + (i + 1) * stride, S.keys, n_first, qop, qlds, nq, st, lane, kr0, kr1);
+    {
+      const int kb = first + (i + 1) * stride;
+      if (kb + 32 > n_first)
+        sub_block<QPW, true>(slotB, kb, S.keys, false, qop, qlds, nq, st, lane, kr0);
+      else
+        sub_block<QPW, false>(slotB, kb, S.keys, false, qop, qlds, nq, st, lane, kr0);
+    }
   }
+  // column sums and true maxima (the four lanes of a column hold its keys
+  // 8G..8G+7 of every sub-block; their bases are equal)
+  const float c = kScale * kLog2e;
 #pragma unroll
-  for (int u = 0; u < QPW; ++u) st.l[u] = add_xor32(add_xor16(st.l[u]));
+  for (int u = 0; u < QPW; ++u) {
+    st.l[u] = add_xor32(add_xor16(st.l[u]));
+    const uint32_t pc = umax_xor32(umax_xor16(st.pm[u]));
+    st.pm[u] = pc;
+    st.mtrue[u] = (pc == 0u) ? ninf : st.mref[u] + __builtin_amdgcn_logf(__uint_as_float(pc)) / c;
+  }
   __syncthreads();  // the rings are reused for the fold
 
   // fold the waves' states in wave order through LDS
@@ -401,7 +484,6 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
 
   // records: o = acc / l (any exponent base), then (true max in score units,
   // l taken to the true max)
-  const float c = kScale * kLog2e;
 #pragma unroll
   for (int u = 0; u < QPW; ++u) {
     const int q = u * 16 + c16;
