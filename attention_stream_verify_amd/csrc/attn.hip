@@ -292,26 +292,58 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, boo
   }
 }
 
+// One q tile's state as the waves fold it at the end: o accumulators, the
+// exponent base, the true max and l at the base.
+struct TileState {
+  f32x4 acc[4];
+  float mref, mtrue, l;
+};
+
 // Fold state b into a (a first, then b: the order is fixed).
-template <int QPW>
-__device__ __forceinline__ void fold(WaveState<QPW>& a, float mref_b, float mtrue_b, float l_b,
-                                     const f32x4* acc_b, int u) {
+__device__ __forceinline__ void fold(TileState& a, const TileState& b) {
   const float c = kScale * kLog2e;
   const float ninf = -__builtin_inff();
-  const float mn = fmaxf(a.mref[u], mref_b);
+  const float mn = fmaxf(a.mref, b.mref);
   const float base = (mn == ninf) ? 0.f : mn;
-  const float a0 = exp2_((a.mref[u] - base) * c);
-  const float a1 = exp2_((mref_b - base) * c);
-  a.mref[u] = mn;
-  a.mtrue[u] = fmaxf(a.mtrue[u], mtrue_b);
-  a.l[u] = __builtin_fmaf(l_b, a1, a.l[u] * a0);
+  const float a0 = exp2_((a.mref - base) * c);
+  const float a1 = exp2_((b.mref - base) * c);
+  a.mref = mn;
+  a.mtrue = fmaxf(a.mtrue, b.mtrue);
+  a.l = __builtin_fmaf(b.l, a1, a.l * a0);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     f32x4 r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = __builtin_fmaf(acc_b[dt][i], a1, a.acc[dt][u][i] * a0);
-    a.acc[dt][u] = r;
+    for (int i = 0; i < 4; ++i) r[i] = __builtin_fmaf(b.acc[dt][i], a1, a.acc[dt][i] * a0);
+    a.acc[dt] = r;
   }
+}
+
+template <int QPW>
+__device__ __forceinline__ TileState tile_of(const WaveState<QPW>& st, int u) {
+  return TileState{{st.acc[0][u], st.acc[1][u], st.acc[2][u], st.acc[3][u]}, st.mref[u], st.mtrue[u], st.l[u]};
+}
+
+// A published tile state in LDS: per lane 4 f32x4 of o, then mref, mtrue, l
+// (lane-major arrays, so every access is one conflict-free LDS op).
+constexpr int kTileFloats = 19 * 64;
+
+__device__ __forceinline__ void put_tile(float* slot, const TileState& t, int lane) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(slot + (dt * 64 + lane) * 4) = t.acc[dt];
+  slot[1024 + lane] = t.mref;
+  slot[1088 + lane] = t.mtrue;
+  slot[1152 + lane] = t.l;
+}
+
+__device__ __forceinline__ TileState get_tile(const float* slot, int lane) {
+  TileState t;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) t.acc[dt] = *reinterpret_cast<const f32x4*>(slot + (dt * 64 + lane) * 4);
+  t.mref = slot[1024 + lane];
+  t.mtrue = slot[1088 + lane];
+  t.l = slot[1152 + lane];
+  return t;
 }
 
 // A block of 4 waves runs one work item; every wave holds all QPW q tiles
@@ -453,57 +485,49 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
   }
   __syncthreads();  // the rings are reused for the fold
 
-  // fold the waves' states in wave order through LDS
-  float* fl = reinterpret_cast<float*>(ringA);
-  constexpr int kSlot = QPW * 64 * 19;  // mref, mtrue, l, then 4 x QPW f32x4 per lane
-  if (wave > 0) {
-    float* my = fl + (wave - 1) * kSlot;
+  // Fold: wave u (u < QPW) owns q tile u. Every wave publishes the states of
+  // the tiles it does not own (at most 12 slots of 4,864 bytes: six in each
+  // ring array), then wave u folds tile u over waves 0, 1, 2, 3 in that order
+  // and writes its records.
+  constexpr int kPer = (QPW == 4) ? 3 : QPW;  // slots a wave publishes
+  auto slot = [&](int w, int u) -> float* {
+    const int i = w * kPer + ((QPW == 4 && u > w) ? u - 1 : u);
+    char* base = (i < 6) ? ringA : ringB;
+    return reinterpret_cast<float*>(base + (i % 6) * kTileFloats * 4);
+  };
+  static_assert(6 * kTileFloats * 4 <= kWaves * kSubBytes, "published states fit the ring");
 #pragma unroll
-    for (int u = 0; u < QPW; ++u) {
-      my[u * 64 + lane] = st.mref[u];
-      my[(QPW + u) * 64 + lane] = st.mtrue[u];
-      my[(2 * QPW + u) * 64 + lane] = st.l[u];
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        *reinterpret_cast<f32x4*>(my + 3 * QPW * 64 + ((dt * QPW + u) * 64 + lane) * 4) = st.acc[dt][u];
-    }
-  }
+  for (int u = 0; u < QPW; ++u)
+    if (u != wave) put_tile(slot(wave, u), tile_of(st, u), lane);
   __syncthreads();
-  if (wave != 0) return;
-  for (int w = 1; w < kWaves; ++w) {
-    const float* o = fl + (w - 1) * kSlot;
+  if (wave >= QPW) return;
+  const int u = wave;
+  TileState own;
 #pragma unroll
-    for (int u = 0; u < QPW; ++u) {
-      f32x4 accb[4];
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        accb[dt] = *reinterpret_cast<const f32x4*>(o + 3 * QPW * 64 + ((dt * QPW + u) * 64 + lane) * 4);
-      fold<QPW>(st, o[u * 64 + lane], o[(QPW + u) * 64 + lane], o[(2 * QPW + u) * 64 + lane], accb, u);
-    }
-  }
+  for (int t = 0; t < QPW; ++t)
+    if (t == u) own = tile_of(st, t);
+  TileState a = (u == 0) ? own : get_tile(slot(0, u), lane);
+  for (int w = 1; w < kWaves; ++w) fold(a, (w == u) ? own : get_tile(slot(w, u), lane));
 
   // records: o = acc / l (any exponent base), then (true max in score units,
   // l taken to the true max)
+  const int q = u * 16 + c16;
+  const int rt = q >> 2;
+  if (rt >= T.nrows) return;
+  const int64_t rec =
+      S.poff + (int64_t(wk.split) * S.rows + T.pos0 + rt) * ASV_Q_HEADS + g * 4 + (q & 3);
+  const float L = a.l;
 #pragma unroll
-  for (int u = 0; u < QPW; ++u) {
-    const int q = u * 16 + c16;
-    const int rt = q >> 2;
-    if (rt >= T.nrows) continue;
-    const int64_t rec =
-        S.poff + (int64_t(wk.split) * S.rows + T.pos0 + rt) * ASV_Q_HEADS + g * 4 + (q & 3);
-    const float L = st.l[u];
+  for (int dt = 0; dt < 4; ++dt) {
+    f32x4 r;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      f32x4 r;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = (L > 0.f) ? st.acc[dt][u][i] / L : 0.f;
-      store16f(po + rec * ASV_HEAD_DIM + dt * 16 + 4 * G, r);
-    }
-    if (G == 0) {
-      const float mt = st.mtrue[u];
-      const float lt = (mt == ninf) ? 0.f : L * exp2_((st.mref[u] - mt) * c);
-      gstore(reinterpret_cast<float2*>(pml) + rec, make_float2((mt == ninf) ? ninf : mt * kScale, lt));
-    }
+    for (int i = 0; i < 4; ++i) r[i] = (L > 0.f) ? a.acc[dt][i] / L : 0.f;
+    store16f(po + rec * ASV_HEAD_DIM + dt * 16 + 4 * G, r);
+  }
+  if (G == 0) {
+    const float mt = a.mtrue;
+    const float lt = (mt == ninf) ? 0.f : L * exp2_((a.mref - mt) * c);
+    gstore(reinterpret_cast<float2*>(pml) + rec, make_float2((mt == ninf) ? ninf : mt * kScale, lt));
   }
 }
 
