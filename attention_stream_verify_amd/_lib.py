@@ -142,6 +142,28 @@ def _ptr_array(rows):
     return arr
 
 
+def time_table_build(streams, conv_state=(), k_cache=(), v_cache=(), reps=20):
+    """Average host time of one asv_seg_table_build call, in microseconds:
+    the arguments are marshalled once, then the C call alone is timed."""
+    import time
+    L = lib()
+    S = len(streams)
+    descs = (StreamDesc * max(1, S))(*[StreamDesc(int(w), int(k), int(c)) for (w, k, c) in streams])
+    n_conv, n_attn = len(conv_state), len(k_cache)
+    cs = _ptr_array(conv_state) if n_conv else None
+    kp = _ptr_array(k_cache) if n_attn else None
+    vv = _ptr_array(v_cache) if n_attn else None
+    info = TableInfo()
+    _check(L.asv_seg_table_build(descs, S, cs, n_conv, kp, vv, n_attn, None, 0,
+                                 ctypes.byref(info)), "asv_seg_table_build")
+    blob = np.zeros(int(info.blob_bytes), dtype=np.uint8)
+    addr, nbytes = blob.ctypes.data, blob.nbytes
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        L.asv_seg_table_build(descs, S, cs, n_conv, kp, vv, n_attn, addr, nbytes, ctypes.byref(info))
+    return (time.perf_counter() - t0) / reps * 1e6
+
+
 def seg_table_build(streams, conv_state=(), k_cache=(), v_cache=(), blob=None):
     """Build the round's table on the host.
 

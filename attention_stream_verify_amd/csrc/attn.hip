@@ -1,9 +1,10 @@
-// Split-K GQA attention over every stream of a shared round, and the merge
-// of each row's split partials (gfx950).
+// Split-K GQA attention over every stream of a shared round (gfx950); the
+// merge of each row's split partials is in merge.hip.
 //
 // PR #1377 "LFM2: shared-round decode", shared-round commit: one attention
 // launch a layer covers every stream's rows through the segment table; each
-// stream's partials are held apart in the scratch; one merge launch follows.
+// stream's partials are held apart in the scratch; one merge launch follows
+// (merge.hip).
 // The per-record arithmetic is written out in include/asv.h.
 //
 // Work item = (16-row tile, kv head, split), one 256-thread block each. A
@@ -569,60 +570,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split(TableView tv, int laye
   attn_item<1, 0>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
 }
 
-// Merge: one wave per (row, q head); lane d owns output dim d. The wave
-// first takes M = max_t m_t over the row's splits (lanes over splits), then
-// every lane walks the splits in order, t = 0, 1, ..., adding
-// w_t = e^(m_t - M) l_t and w_t o_t[d]; the loads of successive splits are
-// independent, so they stay in flight together.
-constexpr int kMergeWaves = 4;
-
-__device__ __forceinline__ float wave_max(float x) {
-  x = max_xor32(max_xor16(x));
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 16));
-  return x;
-}
-
-__global__ __launch_bounds__(64 * kMergeWaves) void merge_rows(TableView tv,
-                                                               const float* __restrict__ po,
-                                                               const float* __restrict__ pml,
-                                                               uint16_t* __restrict__ O) {
-  const int pair = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
-  if (pair >= tv.n_rows * ASV_Q_HEADS) return;
-  const int lane = threadIdx.x & 63;
-  const int r = pair / ASV_Q_HEADS;
-  const int h = pair - r * ASV_Q_HEADS;
-  const asv_row row = uniform(cload(tv.rows + r));
-  const asv_seg S = uniform(cload(tv.segs + row.stream));
-  const int nt = (row.nkeys + S.split_keys - 1) / S.split_keys;
-  const int64_t rec0 = S.poff + int64_t(row.pos) * ASV_Q_HEADS + h;
-  const int64_t step = int64_t(S.rows) * ASV_Q_HEADS;
-  const float2* ml = reinterpret_cast<const float2*>(pml);
-  const float ninf = -__builtin_inff();
-
-  float M = ninf;
-  for (int t = lane; t < nt; t += 64) {
-    const float2 v = gload(ml + rec0 + t * step);
-    if (v.y != 0.f) M = fmaxf(M, v.x);  // empty splits (l = 0) take no part
-  }
-  M = wave_max(M);
-
-  float L = 0.f, acc = 0.f;
-  const float* o = po + rec0 * ASV_HEAD_DIM + lane;
-  const int64_t ostep = step * ASV_HEAD_DIM;
-#pragma unroll 4
-  for (int t = 0; t < nt; ++t) {
-    const float2 v = gload(ml + rec0 + t * step);
-    const float ot = gload(o + t * ostep);
-    if (v.y == 0.f) continue;  // empty split; a NaN partial falls through and propagates
-    const float w = exp2_((v.x - M) * kLog2e) * v.y;
-    L += w;
-    acc = __builtin_fmaf(w, ot, acc);
-  }
-  const float y = (L != 0.f) ? acc / L : 0.f;
-  gstore(O + (int64_t(r) * ASV_Q_HEADS + h) * ASV_HEAD_DIM + lane, uint16_t(f32_to_bf16(y)));
-}
-
 }  // namespace
 }  // namespace asv
 
@@ -649,18 +596,3 @@ extern "C" int asv_shared_attn(const asv_table_info* info, const void* dev_blob,
   return hipGetLastError() == hipSuccess ? ASV_OK : ASV_E_HIP;
 }
 
-extern "C" int asv_attn_merge(const asv_table_info* info, const void* dev_blob,
-                              const float* partials, uint16_t* o, void* stream) {
-  if (!asv::info_ok(info) || dev_blob == nullptr || partials == nullptr || o == nullptr)
-    return ASV_E_ARG;
-  if (!asv::aligned16(dev_blob) || !asv::aligned16(partials) || !asv::aligned16(o))
-    return ASV_E_ARG;
-  const asv::TableView tv = asv::make_view(*info, dev_blob);
-  const float* po = partials;
-  const float* pml = partials + info->partial_count * ASV_HEAD_DIM;
-  const unsigned pairs = unsigned(info->n_rows) * ASV_Q_HEADS;
-  hipLaunchKernelGGL(asv::merge_rows, dim3((pairs + asv::kMergeWaves - 1) / asv::kMergeWaves),
-                     dim3(64 * asv::kMergeWaves), 0,
-                     static_cast<hipStream_t>(stream), tv, po, pml, o);
-  return hipGetLastError() == hipSuccess ? ASV_OK : ASV_E_HIP;
-}

@@ -6,10 +6,15 @@ attention + merge) and the argmax over 128,000-wide logits, every layer on
 its own buffers. Default workload: long context, 4 streams x 16 window rows
 (64 rows) with 65,536 / 98,304 / 130,816 / 131,072 keys.
 
-Prints one JSON line: verify rows/s per round; the roofline of the attention
-kernel (algorithmic K/V + Q bytes per launch over its average launch time,
-timed with HIP events on the stream it runs on, against 8 TB/s); and the CPU
-oracle timed on a bounded sample of the same workload.
+Prints one JSON line: verify rows/s per round (and the round time's median,
+p10 and p90); the roofline of the attention kernel (algorithmic K/V + Q bytes
+per launch over its average launch time, timed with HIP events on the stream
+it runs on, against 8 TB/s); attention + merge per layer (K/V + Q + O bytes
+over the pair's time; alternate rounds time the pair with no event between
+the two kernels and the attention alone); the profiled HBM traffic and MFMA
+busy fraction when profiles/ holds them for these kernel sources; the host
+table build time; and the CPU oracle timed on a bounded sample of the same
+workload.
 """
 
 import argparse
@@ -67,25 +72,44 @@ def profiled_traffic(config):
     (FETCH_SIZE and WRITE_SIZE passes, scaled by a plain-copy calibration),
     as recorded in profiles/ -- or None when there is no profile for this
     workload or the kernel sources changed since it was taken."""
+    f = profile_fields(TRAFFIC_PROFILES.get(config), ("traffic_bytes_per_launch",))
+    return None if f is None else int(f["traffic_bytes_per_launch"])
+
+
+SQ_PROFILES = {3: "profiles/attn_split_long_context_sq_counters.md"}
+
+
+def profile_fields(name, keys):
+    """Fields of a profile summary in profiles/, or None when it is missing or
+    the kernel sources changed since it was taken (their sha256 is recorded)."""
     import hashlib
-    name = TRAFFIC_PROFILES.get(config)
     if name is None or not os.path.exists(os.path.join(ROOT, name)):
         return None
     fields = {}
     for line in open(os.path.join(ROOT, name)):
-        if ":" in line and line.split(":", 1)[0].strip() in (
-                "traffic_bytes_per_launch", "kernel_sources_sha256", "kernel_sources"):
+        if ":" in line and line.split(":", 1)[0].strip() in keys + ("kernel_sources_sha256",
+                                                                   "kernel_sources"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if len(fields) != 3:
+    if "kernel_sources" not in fields or "kernel_sources_sha256" not in fields:
         return None
     h = hashlib.sha256()
     for src in fields["kernel_sources"].split():
         with open(os.path.join(ROOT, src), "rb") as f:
             h.update(f.read())
-    if h.hexdigest() != fields["kernel_sources_sha256"]:
+    if h.hexdigest() != fields["kernel_sources_sha256"] or any(k not in fields for k in keys):
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    return fields
+
+
+def profiled_mfma(config):
+    """MFMA pipe busy fraction of the attention kernel from SQ counters
+    (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles), as recorded in profiles/."""
+    f = profile_fields(SQ_PROFILES.get(config), ("mfma_busy_frac", "valu_active_frac"))
+    if f is None:
+        return None
+    return {"mfma_busy_frac": float(f["mfma_busy_frac"]), "valu_active_frac": float(f["valu_active_frac"]),
+            "source": SQ_PROFILES[config]}
 
 
 def layer_order(n_conv, n_attn):
@@ -175,7 +199,19 @@ def main():
     attn_bytes = 2048 * sum_keys + 4096 * R            # K/V once + Q, per launch
     merge_bytes = 4096 * R                              # O written (partials are a means)
 
-    def step(ev=None):
+    def event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def step(ev=None, split=False):
+        """One round. With ev, records events on torch's current stream (the
+        stream the library launches on): round start, then per attention
+        layer either (attention start, attention end) when split, or
+        (attention start, merge end) -- no event between the two kernels --
+        and the round end."""
+        if ev is not None:
+            ev.append([event()])
         rb.upload()
         for kind, i in order:
             if kind == "conv":
@@ -183,32 +219,50 @@ def main():
                 rb.conv(i, X, W)
             else:
                 if ev is not None:
-                    ev.append(torch.cuda.Event(enable_timing=True))
-                    ev[-1].record()
+                    ev[-1].append(event())
                 rb.attn(i, rnd.attn[i][0])
-                if ev is not None:
-                    ev.append(torch.cuda.Event(enable_timing=True))
-                    ev[-1].record()
+                if ev is not None and split:
+                    ev[-1].append(event())
                 rb.merge()
+                if ev is not None and not split:
+                    ev[-1].append(event())
         rb.argmax(rnd.logits)
+        if ev is not None:
+            ev[-1].append(event())
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    attn_ev = []
+    ev = []
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for _ in range(args.steps):
-        step(attn_ev)
+    for k in range(args.steps):
+        step(ev, split=(k % 2 == 1))
     stop.record()
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
-    attn_ms = [attn_ev[i].elapsed_time(attn_ev[i + 1]) for i in range(0, len(attn_ev), 2)]
+    round_ms = sorted(e[0].elapsed_time(e[-1]) for e in ev)
+    attn_ms, pair_ms = [], []
+    for k, e in enumerate(ev):
+        for j in range(1, len(e) - 1, 2):
+            (attn_ms if k % 2 == 1 else pair_ms).append(e[j].elapsed_time(e[j + 1]))
+    if not attn_ms:  # a single timed round: time attention alone in it
+        attn_ms = pair_ms
     attn_avg_ms = sum(attn_ms) / len(attn_ms)
+    pair_avg_ms = sum(pair_ms) / len(pair_ms)
     achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+
+    def pct(xs, q):
+        return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+
+    # host table build, timed on its own (pure host code, no HIP calls)
+    from attention_stream_verify_amd import _lib
+    build_us = _lib.time_table_build(rnd.streams, [layer[2] for layer in rnd.conv],
+                                     [layer[1] for layer in rnd.attn],
+                                     [layer[2] for layer in rnd.attn])
 
     line = {
         "metric": "verify rows/sec per shared round (conv+attn+argmax); attn HBM GB/s vs peak",
@@ -244,7 +298,16 @@ def main():
             "bytes_per_launch": attn_bytes,
             "avg_launch_us": attn_avg_ms * 1e3,
         },
-        "attn_merge_bytes_per_layer": attn_bytes + merge_bytes,
+        "round_ms": {"median": round_ms[len(round_ms) // 2], "p10": pct(round_ms, 0.1),
+                     "p90": pct(round_ms, 0.9)},
+        "attn_merge": {
+            "bytes_per_layer": attn_bytes + merge_bytes,
+            "avg_pair_us": pair_avg_ms * 1e3,
+            "achieved_gbs": (attn_bytes + merge_bytes) / (pair_avg_ms * 1e-3) / 1e9,
+            "frac": (attn_bytes + merge_bytes) / (pair_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        },
+        "mfma_busy": profiled_mfma(args.config),
+        "table_build_host_us": build_us,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
