@@ -31,7 +31,8 @@ OK, E_ARG, E_SHAPE, E_UNSUPPORTED, E_CAPACITY, E_HIP = 0, -1, -2, -3, -4, -5
 
 # every entry point include/asv.h declares
 SYMBOLS = [
-    "asv_abi_version", "asv_strerror", "asv_seg_table_build", "asv_table_upload",
+    "asv_abi_version", "asv_strerror", "asv_seg_table_build", "asv_block_table_build",
+    "asv_table_upload",
     "asv_shared_conv", "asv_shared_attn", "asv_attn_merge", "asv_row_argmax_workspace",
     "asv_row_argmax",
 ]
@@ -88,6 +89,8 @@ def lib():
         L.asv_seg_table_build.argtypes = [ctypes.POINTER(StreamDesc), i32, ctypes.POINTER(vp), i32,
                                           ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, sz,
                                           ctypes.POINTER(TableInfo)]
+        L.asv_block_table_build.restype = ctypes.c_int
+        L.asv_block_table_build.argtypes = L.asv_seg_table_build.argtypes
         L.asv_table_upload.restype = ctypes.c_int
         L.asv_table_upload.argtypes = [vp, sz, vp, vp]
         L.asv_shared_conv.restype = ctypes.c_int
@@ -142,11 +145,12 @@ def _ptr_array(rows):
     return arr
 
 
-def time_table_build(streams, conv_state=(), k_cache=(), v_cache=(), reps=20):
-    """Average host time of one asv_seg_table_build call, in microseconds:
-    the arguments are marshalled once, then the C call alone is timed."""
+def time_table_build(streams, conv_state=(), k_cache=(), v_cache=(), reps=20, full=False):
+    """Average host time of one table build call, in microseconds: the
+    arguments are marshalled once, then the C call alone is timed."""
     import time
     L = lib()
+    build = L.asv_block_table_build if full else L.asv_seg_table_build
     S = len(streams)
     descs = (StreamDesc * max(1, S))(*[StreamDesc(int(w), int(k), int(c)) for (w, k, c) in streams])
     n_conv, n_attn = len(conv_state), len(k_cache)
@@ -154,18 +158,18 @@ def time_table_build(streams, conv_state=(), k_cache=(), v_cache=(), reps=20):
     kp = _ptr_array(k_cache) if n_attn else None
     vv = _ptr_array(v_cache) if n_attn else None
     info = TableInfo()
-    _check(L.asv_seg_table_build(descs, S, cs, n_conv, kp, vv, n_attn, None, 0,
-                                 ctypes.byref(info)), "asv_seg_table_build")
+    _check(build(descs, S, cs, n_conv, kp, vv, n_attn, None, 0, ctypes.byref(info)), "table build")
     blob = np.zeros(int(info.blob_bytes), dtype=np.uint8)
     addr, nbytes = blob.ctypes.data, blob.nbytes
     t0 = time.perf_counter()
     for _ in range(reps):
-        L.asv_seg_table_build(descs, S, cs, n_conv, kp, vv, n_attn, addr, nbytes, ctypes.byref(info))
+        build(descs, S, cs, n_conv, kp, vv, n_attn, addr, nbytes, ctypes.byref(info))
     return (time.perf_counter() - t0) / reps * 1e6
 
 
-def seg_table_build(streams, conv_state=(), k_cache=(), v_cache=(), blob=None):
-    """Build the round's table on the host.
+def seg_table_build(streams, conv_state=(), k_cache=(), v_cache=(), blob=None, full=False):
+    """Build the round's table on the host (full: block attention, every row
+    seeing all of its stream's keys -- asv_block_table_build).
 
     streams: [(rows, key_count, kv_capacity)]; conv_state / k_cache / v_cache:
     per layer, a list with one tensor (or device address) per stream.
@@ -174,6 +178,8 @@ def seg_table_build(streams, conv_state=(), k_cache=(), v_cache=(), blob=None):
     CPU tensor).
     """
     L = lib()
+    build = L.asv_block_table_build if full else L.asv_seg_table_build
+    name = "asv_block_table_build" if full else "asv_seg_table_build"
     S = len(streams)
     descs = (StreamDesc * max(1, S))(*[StreamDesc(int(w), int(k), int(c)) for (w, k, c) in streams])
     n_conv, n_attn = len(conv_state), len(k_cache)
@@ -183,16 +189,14 @@ def seg_table_build(streams, conv_state=(), k_cache=(), v_cache=(), blob=None):
     kp = _ptr_array(k_cache) if n_attn else None
     vv = _ptr_array(v_cache) if n_attn else None
     info = TableInfo()
-    _check(L.asv_seg_table_build(descs, S, cs, n_conv, kp, vv, n_attn, None, 0,
-                                 ctypes.byref(info)), "asv_seg_table_build")
+    _check(build(descs, S, cs, n_conv, kp, vv, n_attn, None, 0, ctypes.byref(info)), name)
     if blob is None:
         blob = np.zeros(int(info.blob_bytes), dtype=np.uint8)
     if isinstance(blob, np.ndarray):
         addr, nbytes = blob.ctypes.data, blob.nbytes
     else:
         addr, nbytes = int(blob.data_ptr()), blob.numel() * blob.element_size()
-    _check(L.asv_seg_table_build(descs, S, cs, n_conv, kp, vv, n_attn, addr, nbytes,
-                                 ctypes.byref(info)), "asv_seg_table_build")
+    _check(build(descs, S, cs, n_conv, kp, vv, n_attn, addr, nbytes, ctypes.byref(info)), name)
     return info, blob
 
 

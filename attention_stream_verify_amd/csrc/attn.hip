@@ -363,10 +363,12 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
   const asv_tile T = uniform(cload(tv.tiles + wk.tile));
   const asv_seg S = uniform(cload(tv.segs + T.stream));
   const int g = wk.head;
-  const int base_n = S.keys - S.rows + T.pos0;  // tile row i sees base_n + i + 1 keys
-  const int n_first = base_n + 1;
+  // visible key counts come from the table's rows (causal: the tile's first
+  // row sees the fewest; block tables: every row sees all keys)
+  const int n_first = uni(cload(tv.rows + T.row0).nkeys);
+  const int n_last = uni(cload(tv.rows + T.row0 + T.nrows - 1).nkeys);
   const int k0 = wk.split * S.split_keys;
-  const int k1 = min(k0 + S.split_keys, base_n + T.nrows);
+  const int k1 = min(k0 + S.split_keys, n_last);
   const int64_t head_elems = int64_t(S.cap) * ASV_HEAD_DIM;
   const int64_t sel = int64_t(layer) * tv.n_streams + T.stream;
   const uint16_t* Kh = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.kp + sel))) + g * head_elems;
@@ -411,7 +413,7 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
         qop[u][0] = load16(q_ptr(u));
         qop[u][1] = load16(q_ptr(u) + 32);
       }
-      nq[u] = base_n + rt + 1;
+      nq[u] = gload(tv.rows + T.row0 + rt).nkeys;
     } else {
       if constexpr (!q_in_lds<QPW>()) {
         qop[u][0] = u32x4{0u, 0u, 0u, 0u};

@@ -52,11 +52,13 @@ extern "C" const char* asv_strerror(int code) {
   }
 }
 
-extern "C" int asv_seg_table_build(const asv_stream_desc* streams, int32_t n_streams,
-                                   const void* const* conv_state, int32_t n_conv_layers,
-                                   const void* const* k_cache, const void* const* v_cache,
-                                   int32_t n_attn_layers, void* blob, size_t blob_bytes,
-                                   asv_table_info* info) {
+namespace {
+
+// full: block mode, every row seeing all of its stream's keys.
+int build_table(const asv_stream_desc* streams, int32_t n_streams, const void* const* conv_state,
+                int32_t n_conv_layers, const void* const* k_cache, const void* const* v_cache,
+                int32_t n_attn_layers, void* blob, size_t blob_bytes, asv_table_info* info,
+                bool full) {
   if (streams == nullptr || info == nullptr) return ASV_E_ARG;
   if (n_streams < 1 || n_conv_layers < 0 || n_attn_layers < 0) return ASV_E_SHAPE;
 
@@ -133,7 +135,7 @@ extern "C" int asv_seg_table_build(const asv_stream_desc* streams, int32_t n_str
         asv_row& r = rows[t.row0 + i];
         r.stream = s;
         r.pos = p + i;
-        r.nkeys = d.key_count - d.rows + p + i + 1;
+        r.nkeys = full ? d.key_count : d.key_count - d.rows + p + i + 1;
         r.tile = static_cast<int32_t>(tiles.size());
       }
       tiles.push_back(t);
@@ -147,7 +149,7 @@ extern "C" int asv_seg_table_build(const asv_stream_desc* streams, int32_t n_str
   for (int32_t ti = 0; ti < static_cast<int32_t>(tiles.size()); ++ti) {
     const asv_tile& t = tiles[ti];
     const asv_seg& g = segs[t.stream];
-    const int32_t n_last = g.keys - g.rows + t.pos0 + t.nrows;
+    const int32_t n_last = full ? g.keys : g.keys - g.rows + t.pos0 + t.nrows;
     for (int32_t sp = 0; int64_t(sp) * g.split_keys < n_last; ++sp) {
       const int32_t k0 = sp * g.split_keys;
       const int32_t k1 = std::min(k0 + g.split_keys, n_last);
@@ -199,4 +201,24 @@ extern "C" int asv_seg_table_build(const asv_stream_desc* streams, int32_t n_str
     vp[i] = reinterpret_cast<uintptr_t>(v_cache[i]);
   }
   return ASV_OK;
+}
+
+}  // namespace
+
+extern "C" int asv_seg_table_build(const asv_stream_desc* streams, int32_t n_streams,
+                                   const void* const* conv_state, int32_t n_conv_layers,
+                                   const void* const* k_cache, const void* const* v_cache,
+                                   int32_t n_attn_layers, void* blob, size_t blob_bytes,
+                                   asv_table_info* info) {
+  return build_table(streams, n_streams, conv_state, n_conv_layers, k_cache, v_cache,
+                     n_attn_layers, blob, blob_bytes, info, false);
+}
+
+extern "C" int asv_block_table_build(const asv_stream_desc* streams, int32_t n_streams,
+                                     const void* const* conv_state, int32_t n_conv_layers,
+                                     const void* const* k_cache, const void* const* v_cache,
+                                     int32_t n_attn_layers, void* blob, size_t blob_bytes,
+                                     asv_table_info* info) {
+  return build_table(streams, n_streams, conv_state, n_conv_layers, k_cache, v_cache,
+                     n_attn_layers, blob, blob_bytes, info, true);
 }

@@ -17,14 +17,17 @@ class RoundBuffers:
     (layouts of include/asv.h). All tensors must live on ``device``.
     """
 
-    def __init__(self, streams, conv_states, k_caches, v_caches, device="cuda", vocab=None):
+    def __init__(self, streams, conv_states, k_caches, v_caches, device="cuda", vocab=None,
+                 full=False):
         self.streams = [tuple(int(v) for v in s) for s in streams]
         self.device = torch.device(device)
         self._keep = (conv_states, k_caches, v_caches)  # table addresses stay valid
         self.blob_host = None
-        info, blob = _lib.seg_table_build(self.streams, conv_states, k_caches, v_caches)
+        self.full = bool(full)
+        info, blob = _lib.seg_table_build(self.streams, conv_states, k_caches, v_caches, full=full)
         pinned = torch.empty(int(info.blob_bytes), dtype=torch.uint8, pin_memory=True)
-        info, _ = _lib.seg_table_build(self.streams, conv_states, k_caches, v_caches, blob=pinned)
+        info, _ = _lib.seg_table_build(self.streams, conv_states, k_caches, v_caches, blob=pinned,
+                                       full=full)
         self.info = info
         self.blob_host = pinned
         self.blob = torch.empty(int(info.blob_bytes), dtype=torch.uint8, device=self.device)

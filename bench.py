@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=3, choices=[0, 1, 2, 3, 4])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--block", action="store_true",
+                   help="attention through a block table: every row sees all of its stream's keys")
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB three times (the known-size "
@@ -125,7 +127,7 @@ def layer_order(n_conv, n_attn):
     return order
 
 
-def cpu_baseline(rnd, R):
+def cpu_baseline(rnd, R, full=False):
     """The oracle, as it stands, on one conv layer, one attention layer and the
     argmax of this workload, scaled to a round by 30 / 10 / 1."""
     import numpy as np
@@ -151,7 +153,7 @@ def cpu_baseline(rnd, R):
     Qh, Kh = u16(Q), [u16(k) for k in ks]
     Vh = [u16(workloads.v_logical(v)) for v in vs]
     Lh = u16(rnd.logits)
-    t = otable.build(rnd.streams)
+    t = otable.build(rnd.streams, full=full)
     t0 = time.perf_counter()
     oconv.shared_conv(t, Xh, Wh, sth)
     t1 = time.perf_counter()
@@ -193,7 +195,7 @@ def main():
     R, S = rnd.R, rnd.S
     rb = asv.RoundBuffers(rnd.streams, [layer[2] for layer in rnd.conv],
                           [layer[1] for layer in rnd.attn], [layer[2] for layer in rnd.attn],
-                          device=dev, vocab=rnd.logits.shape[1])
+                          device=dev, vocab=rnd.logits.shape[1], full=args.block)
     order = layer_order(rnd.n_conv, rnd.n_attn)
     sum_keys = sum(k for _, k, _ in rnd.streams)
     attn_bytes = 2048 * sum_keys + 4096 * R            # K/V once + Q, per launch
@@ -262,7 +264,7 @@ def main():
     from attention_stream_verify_amd import _lib
     build_us = _lib.time_table_build(rnd.streams, [layer[2] for layer in rnd.conv],
                                      [layer[1] for layer in rnd.attn],
-                                     [layer[2] for layer in rnd.attn])
+                                     [layer[2] for layer in rnd.attn], full=args.block)
 
     line = {
         "metric": "verify rows/sec per shared round (conv+attn+argmax); attn HBM GB/s vs peak",
@@ -278,7 +280,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[args.config],
+            "workload": WORKLOAD_NAMES[args.config] + (", block (non-causal) attention"
+                                                        if args.block else ""),
             "streams": S,
             "rows": R,
             "sum_keys": sum_keys,
@@ -294,7 +297,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": profiled_traffic(args.config),
+            "traffic": None if args.block else profiled_traffic(args.config),
             "bytes_per_launch": attn_bytes,
             "avg_launch_us": attn_avg_ms * 1e3,
         },
@@ -306,12 +309,12 @@ def main():
             "achieved_gbs": (attn_bytes + merge_bytes) / (pair_avg_ms * 1e-3) / 1e9,
             "frac": (attn_bytes + merge_bytes) / (pair_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
-        "mfma_busy": profiled_mfma(args.config),
+        "mfma_busy": None if args.block else profiled_mfma(args.config),
         "table_build_host_us": build_us,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(rnd, R)
+        line["cpu_baseline"] = cpu_baseline(rnd, R, full=args.block)
         line["cpu_baseline"]["gpu_over_cpu"] = line["value"] / line["cpu_baseline"]["value"]
     print(json.dumps(line), flush=True)
 

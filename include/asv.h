@@ -93,7 +93,8 @@ typedef struct {      /* one per stream, caller order                     */
 typedef struct {      /* one per row                                       */
   int32_t stream;
   int32_t pos;        /* row index inside its stream's window             */
-  int32_t nkeys;      /* keys the row sees: keys - rows + pos + 1         */
+  int32_t nkeys;      /* keys the row sees: keys - rows + pos + 1 (causal),
+                         keys (asv_block_table_build)                      */
   int32_t tile;
 } asv_row;
 
@@ -172,6 +173,27 @@ int asv_seg_table_build(const asv_stream_desc* streams, int32_t n_streams,
                         int32_t n_attn_layers, void* blob, size_t blob_bytes,
                         asv_table_info* info);
 
+/* The same table for block (non-causal) attention.
+ *
+ * Defines: PR #1391 "lfm2: draft with LiquidAI's DSpark drafter
+ * (--drafter)", its list of new kernels (the target's attention and merge
+ * with a FULL flag, every block row seeing the keys [0, len + 1), beside the
+ * target's causal instantiations) and the drafter's description (a block of
+ * the pending token and mask tokens attends non-causally). Read as: every row
+ * of stream s sees all K_s keys of its cache, so the window's rows attend to
+ * each other in both directions.
+ *
+ * Arguments, layout, ownership and errors are those of asv_seg_table_build;
+ * the only differences are in the blob: every asv_row has nkeys = key_count,
+ * and the work list holds every split of the stream for every tile.
+ * asv_shared_attn and asv_attn_merge take either table: they read each row's
+ * visible key count from the table. */
+int asv_block_table_build(const asv_stream_desc* streams, int32_t n_streams,
+                          const void* const* conv_state, int32_t n_conv_layers,
+                          const void* const* k_cache, const void* const* v_cache,
+                          int32_t n_attn_layers, void* blob, size_t blob_bytes,
+                          asv_table_info* info);
+
 /* Copy a built blob (host) to dev_blob (device, >= info->blob_bytes,
  * 16-byte aligned) on `stream`. The host blob must stay unchanged until the
  * copy has run (pinned host memory makes the copy asynchronous). */
@@ -204,10 +226,12 @@ int asv_shared_conv(const asv_table_info* info, const void* dev_blob, int32_t la
  *
  * Defines: PR #1377 "LFM2: shared-round decode", shared-round commit (one
  * attention launch a layer over every stream's rows, partials of each stream
- * held apart, checked against float64 attention).
+ * held apart, checked against float64 attention); with a table from
+ * asv_block_table_build, PR #1391's block attention (FULL flag).
  *
  * Row r of stream s, q head h (kv head g = h / 4), split t covering keys
- * [t*S_s, (t+1)*S_s) of the n_r keys the row sees, scores
+ * [t*S_s, (t+1)*S_s) of the n_r keys the row sees (the table's count: causal
+ * from asv_seg_table_build, all K_s from asv_block_table_build), scores
  * s_j = (q . k_j) / 8, writes record p = poff_s + (t*rows_s + pos_r)*32 + h:
  *   o[p][0:64] = sum_j e^(s_j - m) v_j / l,  m = max_j s_j,  l = sum_j e^(s_j - m)
  * (an empty split writes m = -inf, l = 0, o = 0). Keys past a stream's key

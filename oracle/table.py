@@ -24,6 +24,13 @@ definitions (the readings are listed in the design notes):
   (row r, q head h, split t) is poff_s + (t*w_s + pos_r)*32 + h;
 * work items: for every tile, kv head and split that holds a key the tile's
   last row can see.
+
+Block mode (PR #1391 "lfm2: draft with LiquidAI's DSpark drafter
+(--drafter)", its list of new kernels: the target's attention and merge with
+a FULL flag, every block row seeing the keys [0, len + 1)): read as every row
+of a stream seeing all of its K_s keys, n_r = K_s, so the window's rows
+attend to each other both ways; the work items then cover every split of
+the stream for every tile. Everything else is as above.
 """
 
 from dataclasses import dataclass, field
@@ -96,8 +103,9 @@ def validate(streams):
         raise ValueError("more than 2048 rows")
 
 
-def build(streams):
-    """streams: sequence of (rows, key_count, kv_capacity) in caller order."""
+def build(streams, full=False):
+    """streams: sequence of (rows, key_count, kv_capacity) in caller order;
+    full: block mode (every row sees all of its stream's keys)."""
     validate(streams)
     S = len(streams)
     rows = np.array([s[0] for s in streams], dtype=np.int64)
@@ -117,7 +125,7 @@ def build(streams):
             r = seg_off[s] + i
             row_stream[r] = s
             row_pos[r] = i
-            row_nkeys[r] = keys[s] - rows[s] + i + 1
+            row_nkeys[r] = keys[s] if full else keys[s] - rows[s] + i + 1
 
     tiles = []
     for s in range(S):
@@ -139,7 +147,7 @@ def build(streams):
 
     work = []
     for ti, (s, _r0, n, p0) in enumerate(tiles):
-        n_last = keys[s] - rows[s] + p0 + n
+        n_last = keys[s] if full else keys[s] - rows[s] + p0 + n
         for t in range(-(-int(n_last) // int(split[s]))):
             for g in range(N_KV_HEADS):
                 work.append((ti, g, t))

@@ -55,8 +55,9 @@ def check_partials(po, pml, ref_o, ref_m, ref_l, recs, what):
 
 # ----------------------------------------------------------- device rounds
 
-def run_round(rnd, layers_conv=None, layers_attn=None, with_argmax=True):
-    """Run a workloads.Round through the library on the current device.
+def run_round(rnd, layers_conv=None, layers_attn=None, with_argmax=True, full=False):
+    """Run a workloads.Round through the library on the current device
+    (full: with a block attention table).
 
     Returns the RoundBuffers and, per layer, the outputs (cloned)."""
     import attention_stream_verify_amd as asv
@@ -65,7 +66,7 @@ def run_round(rnd, layers_conv=None, layers_attn=None, with_argmax=True):
     vs = [layer[2] for layer in rnd.attn]
     vocab = rnd.logits.shape[1] if (with_argmax and rnd.logits is not None) else None
     rb = asv.RoundBuffers(rnd.streams, convs, ks, vs, device=rnd.attn[0][0].device if rnd.attn else "cuda",
-                          vocab=vocab)
+                          vocab=vocab, full=full)
     rb.upload()
     out = {"y": [], "o": [], "partials": [], "states": []}
     for li in (range(rnd.n_conv) if layers_conv is None else layers_conv):
@@ -106,9 +107,9 @@ def sample_rows(table, n_extra, seed):
     return sorted(rows)
 
 
-def check_attention_layer(rnd, rb, partials, o_bits, li, rows, what):
+def check_attention_layer(rnd, rb, partials, o_bits, li, rows, what, full=False):
     """Compare a layer's partials (every record of `rows`) and merged output."""
-    t = otable.build(rnd.streams)
+    t = otable.build(rnd.streams, full=full)
     Qh, Kh, Vh = oattn_inputs = oracle_attn_inputs(rnd, li)
     del oattn_inputs
     ref_o, ref_m, ref_l, _ = oattn.partials(t, Qh, Kh, Vh, rows=rows)
@@ -126,7 +127,7 @@ def check_attention_layer(rnd, rb, partials, o_bits, li, rows, what):
     for r in rows:
         s = int(t.row_stream[r])
         tile = [tt for tt in t.tiles if tt[1] <= r < tt[1] + tt[2]][0]
-        last = t.keys[s] - t.rows[s] + tile[3] + tile[2]
+        last = t.keys[s] if full else t.keys[s] - t.rows[s] + tile[3] + tile[2]
         for sp in range(t.row_nsplit(r), -(-int(last) // int(t.split[s]))):
             for h in range(32):
                 rec = t.record(r, h, sp)

@@ -48,17 +48,17 @@ def _fake_ptrs(streams, n_layers, nbytes_fn, base):
     return out
 
 
-def _build(streams, n_conv=1, n_attn=1):
+def _build(streams, n_conv=1, n_attn=1, full=False):
     cs = _fake_ptrs(streams, n_conv, lambda s: 8192, 1 << 40)
     kp = _fake_ptrs(streams, n_attn, lambda s: 8 * s[2] * 64 * 2, 1 << 42)
     vp = _fake_ptrs(streams, n_attn, lambda s: 8 * s[2] * 64 * 2, 1 << 44)
-    info, blob = asv.seg_table_build(streams, cs, kp, vp)
+    info, blob = asv.seg_table_build(streams, cs, kp, vp, full=full)
     return info, blob, asv.table_arrays(info, blob), (cs, kp, vp)
 
 
-def _compare(streams):
-    info, blob, t, (cs, kp, vp) = _build(streams)
-    o = otable.build(streams)
+def _compare(streams, full=False):
+    info, blob, t, (cs, kp, vp) = _build(streams, full=full)
+    o = otable.build(streams, full=full)
     S, R = len(streams), o.n_rows
     assert (info.n_streams, info.n_rows, info.n_tiles) == (S, R, len(o.tiles))
     assert info.partial_count == o.partial_count
@@ -85,7 +85,7 @@ def _compare(streams):
     assert all(w["keys"][i] >= w["keys"][i + 1] for i in range(len(w) - 1))
     for ti, h, sp, k in zip(w["tile"], w["head"], w["split"], w["keys"]):
         s, _r0, n, p0 = o.tiles[ti]
-        last = o.keys[s] - o.rows[s] + p0 + n
+        last = o.keys[s] if full else o.keys[s] - o.rows[s] + p0 + n
         assert k == min((sp + 1) * o.split[s], last) - sp * o.split[s] > 0
     assert np.array_equal(t["conv_state"], np.array(cs, dtype=np.uint64).ravel())
     assert np.array_equal(t["k"], np.array(kp, dtype=np.uint64).ravel())
@@ -93,8 +93,9 @@ def _compare(streams):
 
 
 @pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
-def test_table_bit_exact_on_workloads(config):
-    _compare(workloads.streams_for(config))
+@pytest.mark.parametrize("full", [False, True])
+def test_table_bit_exact_on_workloads(config, full):
+    _compare(workloads.streams_for(config), full)
 
 
 _stream = st.integers(1, 600).flatmap(
@@ -105,6 +106,7 @@ _stream = st.integers(1, 600).flatmap(
 @given(st.lists(_stream, min_size=1, max_size=12).filter(lambda s: sum(w for w, _, _ in s) <= 2048))
 def test_table_bit_exact_random(streams):
     _compare(streams)
+    _compare(streams, full=True)
 
 
 def test_size_query_and_capacity():
@@ -162,3 +164,11 @@ def test_tables_without_layers_and_counts_at_1_32_2048_rows():
         info, _ = asv.seg_table_build(streams)
         assert info.n_rows in (1, 32, 2048) and info.partial_count == expect
         assert info.partial_count == otable.build(streams).partial_count
+
+
+def test_block_table_refuses_what_the_causal_one_refuses():
+    bad = [(0, 10, 32)]
+    cs = _fake_ptrs([(1, 10, 32)], 1, lambda s: 8192, 1 << 40)
+    with pytest.raises(asv.AsvError) as e:
+        asv.seg_table_build(bad, cs, [], [], full=True)
+    assert e.value.code == -2

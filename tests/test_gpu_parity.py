@@ -291,3 +291,64 @@ def test_isolation_by_perturbation_and_determinism():
         if s != j:
             assert torch.equal(states[s], base_states[s])
     assert torch.isnan(pert["o"][0][off:off + w].view(torch.bfloat16).float()).all()
+
+
+# ---------------------------------------------------------- block attention
+# Tables from asv_block_table_build: every row sees all of its stream's keys
+# (PR #1391's FULL block attention); same kernels, same bounds.
+
+@pytest.mark.parametrize("config,extra", [(0, 0), (2, 8), (3, 6), (4, 10)])
+def test_block_attention_parity(config, extra):
+    rnd = _round(config, n_conv=0, n_attn=1, with_logits=False)
+    rb, out = run_round(rnd, with_argmax=False, full=True)
+    t = otable.build(rnd.streams, full=True)
+    rows = list(range(t.n_rows)) if config == 0 else sample_rows(t, extra, config)
+    if config == 4:
+        rows = [r for r in rows if t.row_nkeys[r] <= 40000][:40] + \
+               [r for r in rows if t.row_nkeys[r] > 40000][:4]
+    prel, oerr = check_attention_layer(rnd, rb, out["partials"][0], out["o"][0], 0, rows,
+                                       f"block {config}", full=True)
+    print(f"[parity] block workload {config}: {len(rows)} rows, partial o rel err {prel:.2e}, "
+          f"output abs err {oerr:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("streams", [
+    [(1, 1, 32)],                                # one key
+    [(16, 16, 32)],                              # window = whole cache
+    [(3, 40, 64), (16, 4097, 4128), (9, 2049, 2080), (2, 513, 544)],   # ragged splits
+    [(33, 600, 640), (1, 5000, 5024)],           # a 3-tile chunk
+    [(512, 3000, 3072)],                         # a prompt chunk of 32 tiles
+])
+def test_block_attention_edge_shapes(streams):
+    rnd = workloads.Round(0, "cuda", n_conv=0, n_attn=1, streams=streams, with_logits=False)
+    print(f"\n[parity] block attention edge {streams}", flush=True)
+    rb, out = run_round(rnd, with_argmax=False, full=True)
+    t = otable.build(streams, full=True)
+    rows = list(range(t.n_rows)) if t.n_rows <= 64 else sample_rows(t, 24, 5)
+    check_attention_layer(rnd, rb, out["partials"][0], out["o"][0], 0, rows,
+                          f"block edge {streams}", full=True)
+
+
+@pytest.mark.parametrize("config", [2, 4])
+def test_block_shared_round_equals_each_stream_alone(config):
+    rnd = _round(config, n_conv=0, n_attn=1, with_logits=False)
+    rb, out = run_round(rnd, with_argmax=False, full=True)
+    t = otable.build(rnd.streams, full=True)
+    P = int(rb.info.partial_count)
+    po = out["partials"][0][:P * 64].view(P, 64)
+    pml = out["partials"][0][P * 64:].view(P, 2)
+    streams = range(len(rnd.streams)) if config != 4 else [0, 1, 47, 48, len(rnd.streams) - 1]
+    for s in streams:
+        one, off = _slice_round(rnd, s)
+        rb1, out1 = run_round(one, with_argmax=False, full=True)
+        w = rnd.streams[s][0]
+        assert torch.equal(out1["o"][0], out["o"][0][off:off + w])
+        t1 = otable.build([rnd.streams[s]], full=True)
+        P1 = int(rb1.info.partial_count)
+        po1 = out1["partials"][0][:P1 * 64].view(P1, 64)
+        pml1 = out1["partials"][0][P1 * 64:].view(P1, 2)
+        for i in range(w):
+            for sp in range(t1.row_nsplit(i)):
+                a = [t.record(off + i, h, sp) for h in range(32)]
+                b = [t1.record(i, h, sp) for h in range(32)]
+                assert torch.equal(po[a], po1[b]) and torch.equal(pml[a], pml1[b])

@@ -197,3 +197,63 @@ def test_merge_skips_empty_splits_and_propagates_nan():
     pl3 = pl.copy()
     pl3[recs[2]] = np.nan
     assert np.isnan(attn.merge(t, po, pm, pl3)[0, 0]).all()
+
+
+# ------------------------------------------------------------ block attention
+# PR #1391 "lfm2: draft with LiquidAI's DSpark drafter (--drafter)", its list
+# of new kernels: the target's attention with a FULL flag, every block row
+# seeing the keys [0, len + 1); read as every row seeing all K_s keys.
+
+def test_block_matches_torch_sdpa_over_all_keys():
+    streams = [(5, 200, 224), (1, 77, 96), (9, 600, 608)]
+    t, Q, K, V = _round(streams, 11)
+    tb = table.build(streams, full=True)
+    assert all(int(tb.row_nkeys[r]) == streams[int(tb.row_stream[r])][1] for r in range(tb.n_rows))
+    got = attn.attention(tb, Q, K, V)
+    ref = _sdpa_rows(tb, Q, K, V, range(tb.n_rows))
+    for r in range(tb.n_rows):
+        assert np.allclose(got[r], ref[r], rtol=0, atol=1e-12), r
+
+
+def test_block_last_row_and_one_row_windows_equal_causal():
+    streams = [(4, 300, 320), (1, 90, 96), (16, 700, 704)]
+    t, Q, K, V = _round(streams, 12)
+    tb = table.build(streams, full=True)
+    causal = attn.attention(t, Q, K, V)
+    block = attn.attention(tb, Q, K, V)
+    for s in range(len(streams)):
+        last = int(t.seg_off[s + 1]) - 1          # the window's last row sees every key either way
+        assert np.array_equal(block[last], causal[last])
+    one = [(1, 50, 64), (1, 300, 320)]
+    t1 = table.build(one)
+    tb1 = table.build(one, full=True)
+    assert np.array_equal(t1.row_nkeys, tb1.row_nkeys)
+    assert np.array_equal(t1.work, tb1.work)
+
+
+def test_block_rows_with_one_query_agree_and_causal_rows_do_not():
+    streams = [(6, 400, 416)]
+    t, Q, K, V = _round(streams, 13)
+    Q[:] = Q[0]                                    # every row asks the same query
+    tb = table.build(streams, full=True)
+    block = attn.attention(tb, Q, K, V)
+    causal = attn.attention(t, Q, K, V)
+    for r in range(1, 6):
+        assert np.array_equal(block[r], block[0])
+        assert not np.array_equal(causal[r], causal[0])
+
+
+def test_block_keys_past_count_unread_and_partials_merge():
+    streams = [(20, 9000, 9024), (3, 2500, 2560)]
+    t, Q, K, V = _round(streams, 14)
+    tb = table.build(streams, full=True)
+    base = attn.attention(tb, Q, K, V)
+    K2 = [k.copy() for k in K]
+    V2 = [v.copy() for v in V]
+    for s, (_, n, _) in enumerate(streams):
+        K2[s][:, n:] = _bits(50.0)
+        V2[s][:, n:] = _bits(-7.0)
+    assert np.array_equal(attn.attention(tb, Q, K2, V2), base)
+    po, pm, pl, defined = attn.partials(tb, Q, K, V)
+    assert defined.all()                           # every row has every split of its stream
+    assert np.allclose(attn.merge(tb, po, pm, pl), base, rtol=0, atol=1e-12)
