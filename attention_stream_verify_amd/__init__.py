@@ -16,7 +16,7 @@ raises.
 from ._lib import (  # noqa: F401
     ABI_VERSION, CONV_IN, HEAD_DIM, HIDDEN, KEY_BLOCK, KV_HEADS, MAX_KEYS, MAX_ROWS,
     PARTIAL_FLOATS, Q_HEADS, SYMBOLS, TILE_ROWS, AsvError, StreamDesc, TableInfo, abi_version,
-    attn_merge, lib, partial_floats, row_argmax, row_argmax_workspace, seg_table_build,
+    attn_merge, draft_ids, lib, partial_floats, row_argmax, row_argmax_workspace, seg_table_build,
     shared_attn, shared_conv, strerror, table_arrays, table_upload,
 )
 from .runner import RoundBuffers  # noqa: F401

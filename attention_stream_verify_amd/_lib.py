@@ -34,7 +34,7 @@ SYMBOLS = [
     "asv_abi_version", "asv_strerror", "asv_seg_table_build", "asv_block_table_build",
     "asv_table_upload",
     "asv_shared_conv", "asv_shared_attn", "asv_attn_merge", "asv_row_argmax_workspace",
-    "asv_row_argmax",
+    "asv_row_argmax", "asv_draft_ids",
 ]
 
 
@@ -103,6 +103,8 @@ def lib():
         L.asv_row_argmax_workspace.argtypes = [i64, i64]
         L.asv_row_argmax.restype = ctypes.c_int
         L.asv_row_argmax.argtypes = [vp, i64, i64, i64, vp, vp, vp, sz, vp]
+        L.asv_draft_ids.restype = ctypes.c_int
+        L.asv_draft_ids.argtypes = [vp, i32, vp, vp, i64, i64, vp, i64, vp, vp]
         if L.asv_abi_version() != ABI_VERSION:
             raise RuntimeError("libasv.so has a different ABI version than this binding")
         _lib = L
@@ -253,6 +255,14 @@ def row_argmax(logits, rows, vocab, row_stride, pick, flag, workspace, stream=No
     _check(lib().asv_row_argmax(_addr(logits), int(rows), int(vocab), int(row_stride), _addr(pick),
                                 _addr(flag), _addr(workspace), nbytes, _stream(stream)),
            "asv_row_argmax")
+
+
+def draft_ids(spans, n_streams, pick, pick_flag, n_picks, vocab, ids, n_ids, fail, stream=None):
+    """spans: device int32 [n_streams][3] (src, dst, count); the rest device
+    tensors as in include/asv.h."""
+    _check(lib().asv_draft_ids(_addr(spans), int(n_streams), _addr(pick), _addr(pick_flag),
+                               int(n_picks), int(vocab), _addr(ids), int(n_ids), _addr(fail),
+                               _stream(stream)), "asv_draft_ids")
 
 
 def partial_floats(info):

@@ -39,6 +39,13 @@ class RoundBuffers:
         self.pick = torch.empty(R, dtype=torch.int32, device=self.device)
         self.flag = torch.empty(R, dtype=torch.uint8, device=self.device)
         self.vocab = vocab
+        spans, r0 = [], 0
+        for w, _, _ in self.streams:          # each stream's rows of the picks, in place
+            spans.append((r0, r0, w))
+            r0 += w
+        self.spans = torch.tensor(spans, dtype=torch.int32, device=self.device).reshape(-1, 3)
+        self.ids = torch.zeros(R, dtype=torch.int32, device=self.device)
+        self.fail = torch.zeros(len(self.streams), dtype=torch.uint8, device=self.device)
         self.workspace = None
         if vocab is not None:
             nb = _lib.row_argmax_workspace(R, vocab)
@@ -63,6 +70,13 @@ class RoundBuffers:
                                          dtype=torch.uint8, device=self.device)
         stride = vocab if row_stride is None else row_stride
         _lib.row_argmax(logits, logits.shape[0], vocab, stride, self.pick, self.flag, self.workspace)
+
+    def draft(self, vocab=None):
+        """Gather the picks of every stream's rows into ids, with a fail flag
+        per stream (asv_draft_ids)."""
+        vocab = self.vocab if vocab is None else vocab
+        _lib.draft_ids(self.spans, len(self.streams), self.pick, self.flag, self.R, vocab,
+                       self.ids, self.R, self.fail)
 
     def partial_views(self):
         P = int(self.info.partial_count)

@@ -260,6 +260,16 @@ def main():
     def pct(xs, q):
         return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
 
+    # draft-id gather over the round's picks, timed on its own (a few us)
+    rb.draft()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(100):
+        rb.draft()
+    d1.record()
+    torch.cuda.synchronize()
+    draft_us = d0.elapsed_time(d1) * 1e3 / 100
+
     # host table build, timed on its own (pure host code, no HIP calls)
     from attention_stream_verify_amd import _lib
     build_us = _lib.time_table_build(rnd.streams, [layer[2] for layer in rnd.conv],
@@ -311,6 +321,7 @@ def main():
         },
         "mfma_busy": None if args.block else profiled_mfma(args.config),
         "table_build_host_us": build_us,
+        "draft_ids_us": draft_us,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

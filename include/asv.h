@@ -134,6 +134,12 @@ typedef struct {
   int64_t off_v;           /* uint64 device addresses [n_attn_layers][n_streams] */
 } asv_table_info;
 
+typedef struct {      /* one stream's drafts for asv_draft_ids             */
+  int32_t src;        /* first pick of the stream                          */
+  int32_t dst;        /* id slot the first pick goes to                    */
+  int32_t count;      /* picks to copy (0 or less: none)                   */
+} asv_draft_span;
+
 int asv_abi_version(void);
 const char* asv_strerror(int code);
 
@@ -284,6 +290,37 @@ size_t asv_row_argmax_workspace(int64_t rows, int64_t vocab);
 int asv_row_argmax(const uint16_t* logits, int64_t rows, int64_t vocab, int64_t row_stride,
                    int32_t* pick, uint8_t* flag, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/* Copy each stream's drafts from the picks into the verify ids, with a
+ * failure flag per stream.
+ *
+ * Defines: PR #1391 "lfm2: draft with LiquidAI's DSpark drafter
+ * (--drafter)": a kernel copies each window's drafts from the drafter's
+ * picks into the verify's ids, each pick exactly or 0 for a token past the
+ * vocabulary; the held-draft fix adds a flag the verify reads before any
+ * cache commit, so that a NaN, Inf or invalid pick fails (DraftNonfinite).
+ *
+ * For stream s (span = spans[s]) and i < span.count:
+ *   p = pick[span.src + i];  ids[span.dst + i] = (0 <= p < vocab) ? p : 0
+ *   fail[s] = 1 when some p is outside [0, vocab) or pick_flag[span.src + i]
+ *             is set (the argmax saw a NaN or an infinity), else 0.
+ * A span with count <= 0 copies nothing and does not fail. An entry whose
+ * pick or id index falls outside [0, n_picks) or [0, n_ids) fails its
+ * stream and writes nothing. ids outside the spans are untouched. Streams
+ * run in parallel: source ranges may overlap, destination ranges must not
+ * (where they do, which stream's id remains is unspecified).
+ *
+ *   spans      device, asv_draft_span [n_streams], 4-byte aligned
+ *   pick       device, int32 [n_picks] (asv_row_argmax's picks)
+ *   pick_flag  device, uint8 [n_picks] (asv_row_argmax's flags)
+ *   ids        device, int32 [n_ids], written inside the spans only
+ *   fail       device, uint8 [n_streams], all written
+ * Errors: ASV_E_SHAPE for a negative count or size or vocab < 1; ASV_E_ARG
+ * for a null or misaligned pointer; ASV_E_HIP. n_streams == 0 launches
+ * nothing. */
+int asv_draft_ids(const asv_draft_span* spans, int32_t n_streams, const int32_t* pick,
+                  const uint8_t* pick_flag, int64_t n_picks, int64_t vocab, int32_t* ids,
+                  int64_t n_ids, uint8_t* fail, void* stream);
 
 #ifdef __cplusplus
 }

@@ -172,3 +172,13 @@ def test_block_table_refuses_what_the_causal_one_refuses():
     with pytest.raises(asv.AsvError) as e:
         asv.seg_table_build(bad, cs, [], [], full=True)
     assert e.value.code == -2
+
+
+def test_draft_ids_refusals_on_the_host():
+    for args, code in [((None, -1, None, None, 0, 10, None, 0, None), -2),
+                       ((None, 1, None, None, 0, 0, None, 0, None), -2),
+                       ((None, 1, None, None, 5, 10, None, 5, None), -1)]:
+        with pytest.raises(asv.AsvError) as e:
+            asv.draft_ids(*args, stream=0)
+        assert e.value.code == code
+    asv.draft_ids(None, 0, None, None, 0, 10, None, 0, None, stream=0)
