@@ -34,8 +34,13 @@ SYMBOLS = [
     "asv_abi_version", "asv_strerror", "asv_seg_table_build", "asv_block_table_build",
     "asv_table_upload",
     "asv_shared_conv", "asv_shared_attn", "asv_attn_merge", "asv_row_argmax_workspace",
-    "asv_row_argmax", "asv_draft_ids",
+    "asv_row_argmax", "asv_draft_ids", "asv_markov_workspace", "asv_markov_pick",
+    "asv_markov_pack_w2",
 ]
+
+MARKOV_MAX_CHAINS = 32
+MARKOV_MAX_DEPTH = 16
+MARKOV_MAX_RANK = 256
 
 
 class AsvError(RuntimeError):
@@ -47,6 +52,10 @@ class AsvError(RuntimeError):
 class StreamDesc(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int32), ("key_count", ctypes.c_int32),
                 ("kv_capacity", ctypes.c_int32)]
+
+
+class MarkovChain(ctypes.Structure):
+    _fields_ = [("row0", ctypes.c_int32), ("depth", ctypes.c_int32)]
 
 
 class TableInfo(ctypes.Structure):
@@ -105,6 +114,13 @@ def lib():
         L.asv_row_argmax.argtypes = [vp, i64, i64, i64, vp, vp, vp, sz, vp]
         L.asv_draft_ids.restype = ctypes.c_int
         L.asv_draft_ids.argtypes = [vp, i32, vp, vp, i64, i64, vp, i64, vp, vp]
+        L.asv_markov_workspace.restype = sz
+        L.asv_markov_workspace.argtypes = [i64]
+        L.asv_markov_pick.restype = ctypes.c_int
+        L.asv_markov_pick.argtypes = [vp, i64, i64, ctypes.POINTER(MarkovChain), i32, vp, vp, vp,
+                                      i64, i32, vp, vp, vp, sz, vp]
+        L.asv_markov_pack_w2.restype = ctypes.c_int
+        L.asv_markov_pack_w2.argtypes = [vp, i64, i32, vp, vp]
         if L.asv_abi_version() != ABI_VERSION:
             raise RuntimeError("libasv.so has a different ABI version than this binding")
         _lib = L
@@ -268,3 +284,26 @@ def draft_ids(spans, n_streams, pick, pick_flag, n_picks, vocab, ids, n_ids, fai
 def partial_floats(info):
     """floats of the partials buffer asv_shared_attn writes."""
     return int(info.partial_count) * PARTIAL_FLOATS
+
+
+def markov_workspace(vocab):
+    return int(lib().asv_markov_workspace(int(vocab)))
+
+
+def markov_pack_w2(w2, vocab, rank, w2c, stream=None):
+    """W2 [vocab][rank] bf16 -> the chunk-major layout markov_pick reads."""
+    _check(lib().asv_markov_pack_w2(_addr(w2), int(vocab), int(rank), _addr(w2c), _stream(stream)),
+           "asv_markov_pack_w2")
+
+
+def markov_pick(base, rows, row_stride, chains, prev0, w1, w2c, vocab, rank, pick, flag, workspace,
+                stream=None):
+    """chains: host list of (row0, depth); the rest device tensors as in
+    include/asv.h. workspace: a device tensor of markov_workspace(vocab) bytes."""
+    n = len(chains)
+    arr = (MarkovChain * max(1, n))(*[MarkovChain(int(r), int(d)) for (r, d) in chains])
+    nbytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    _check(lib().asv_markov_pick(_addr(base), int(rows), int(row_stride), arr, n, _addr(prev0),
+                                 _addr(w1), _addr(w2c), int(vocab), int(rank), _addr(pick),
+                                 _addr(flag), _addr(workspace), nbytes, _stream(stream)),
+           "asv_markov_pick")

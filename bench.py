@@ -43,6 +43,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=3, choices=[0, 1, 2, 3, 4])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-markov", action="store_true", help="skip the Markov-head timing leg")
     p.add_argument("--block", action="store_true",
                    help="attention through a block table: every row sees all of its stream's keys")
     p.add_argument("--seed", type=int, default=None)
@@ -172,6 +173,49 @@ def cpu_baseline(rnd, R, full=False):
     }
 
 
+def markov_leg(torch, asv, dev, seed, calls=20):
+    """One Markov-head pass of the drafter: 4 chains x depth 8 (a hold pass
+    holds at most 32 rows), vocabulary 128,000, rank 256, random bf16
+    weights. Each depth reads all of W2 once (every chain at that depth
+    shares it) plus each chain's logit row; the W1 rows are 512 bytes each."""
+    vocab, rank, chains = 128000, 256, [(0, 8), (8, 8), (16, 8), (24, 8)]
+    rows = 32
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 101)
+
+    def bf16(shape, scale):
+        x = torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * scale
+        return x.to(torch.bfloat16).view(torch.int16)
+
+    w1, w2, base = bf16((vocab, rank), 0.3), bf16((vocab, rank), 0.3), bf16((rows, vocab), 3.0)
+    w2c = torch.empty_like(w2)
+    asv.markov_pack_w2(w2, vocab, rank, w2c)
+    prev0 = torch.tensor([17, 4242, 90000, 127999], dtype=torch.int32, device=dev)
+    pick = torch.empty(rows, dtype=torch.int32, device=dev)
+    flag = torch.empty(rows, dtype=torch.uint8, device=dev)
+    ws = torch.empty(asv.markov_workspace(vocab), dtype=torch.uint8, device=dev)
+
+    def call():
+        asv.markov_pick(base, rows, vocab, chains, prev0, w1, w2c, vocab, rank, pick, flag, ws)
+
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(calls):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    depth = 8
+    nbytes = depth * vocab * rank * 2 + rows * vocab * 2 + rows * rank * 2
+    return {"shape": "4 chains x depth 8, vocab 128,000, rank 256", "avg_call_us": us,
+            "launches_per_call": 2 * depth, "bytes_per_call": nbytes,
+            "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
+            "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -270,6 +314,8 @@ def main():
     torch.cuda.synchronize()
     draft_us = d0.elapsed_time(d1) * 1e3 / 100
 
+    markov = None if args.no_markov else markov_leg(torch, asv, dev, rnd.seed)
+
     # host table build, timed on its own (pure host code, no HIP calls)
     from attention_stream_verify_amd import _lib
     build_us = _lib.time_table_build(rnd.streams, [layer[2] for layer in rnd.conv],
@@ -322,6 +368,7 @@ def main():
         "mfma_busy": None if args.block else profiled_mfma(args.config),
         "table_build_host_us": build_us,
         "draft_ids_us": draft_us,
+        "markov": markov,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

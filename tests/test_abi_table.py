@@ -182,3 +182,32 @@ def test_draft_ids_refusals_on_the_host():
             asv.draft_ids(*args, stream=0)
         assert e.value.code == code
     asv.draft_ids(None, 0, None, None, 0, 10, None, 0, None, stream=0)
+
+
+def test_markov_refusals_on_the_host():
+    """Every refusal happens before a launch (fake, aligned device addresses)."""
+    A = 1 << 20
+    ok = dict(base=A, rows=8, row_stride=1000, chains=[(0, 4), (4, 4)], prev0=A, w1=A, w2c=A,
+              vocab=1000, rank=64, pick=A, flag=A)
+    ws = asv.markov_workspace(1000)
+    assert ws >= 4 * 32 * 16
+
+    def call(workspace_bytes=ws, **kw):
+        a = dict(ok, **kw)
+        L = asv.lib()
+        arr = (asv.MarkovChain * max(1, len(a["chains"])))(*[asv.MarkovChain(r, d) for r, d in a["chains"]])
+        return L.asv_markov_pick(a["base"], a["rows"], a["row_stride"], arr, len(a["chains"]),
+                                 a["prev0"], a["w1"], a["w2c"], a["vocab"], a["rank"], a["pick"],
+                                 a["flag"], A, workspace_bytes, 0)
+
+    assert call(rank=12) == -3 and call(rank=264) == -3 and call(rank=0) == -3
+    assert call(chains=[(0, 0)]) == -2 and call(chains=[(0, 17)], rows=32) == -2
+    assert call(chains=[(0, 4), (3, 2)]) == -2                    # two chains share row 3
+    assert call(chains=[(6, 4)]) == -2                            # past the rows
+    assert call(chains=[(i, 1) for i in range(33)], rows=40) == -2
+    assert call(vocab=0) == -2 and call(row_stride=999) == -2
+    assert call(base=None) == -1 and call(w1=A + 8) == -1
+    assert call(workspace_bytes=ws - 1) == -4
+    assert call(chains=[]) == 0                                   # nothing to do, no launch
+    assert asv.lib().asv_markov_pack_w2(A, 1000, 12, A * 3, 0) == -3
+    assert asv.lib().asv_markov_pack_w2(A, 1000, 64, A + 64, 0) == -1   # overlapping

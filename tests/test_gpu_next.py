@@ -81,3 +81,130 @@ def test_draft_ids_after_row_argmax_with_planted_rows():
 
 def test_draft_ids_zero_streams():
     asv.draft_ids(None, 0, None, None, 0, 10, None, 0, None)   # launches nothing
+
+
+# ---- Markov-head step -------------------------------------------------------
+
+from oracle import markov as omarkov  # noqa: E402
+
+
+def _bf16(rng, shape, scale=1.0):
+    x = rng.standard_normal(shape).astype(np.float32) * np.float32(scale)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _markov_gpu(base, chains, prev0, w1, w2, fill_pick=-7, fill_flag=9):
+    rows, vocab = base.shape
+    rank = w1.shape[1]
+    B = _dev(base.view(np.int16), torch.int16)
+    W1 = _dev(w1.view(np.int16), torch.int16)
+    W2 = _dev(w2.view(np.int16), torch.int16)
+    W2c = torch.empty_like(W2)
+    asv.markov_pack_w2(W2, vocab, rank, W2c)
+    P0 = _dev(np.asarray(prev0, dtype=np.int32), torch.int32)
+    pick = torch.full((rows,), fill_pick, dtype=torch.int32, device="cuda")
+    flag = torch.full((rows,), fill_flag, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(asv.markov_workspace(vocab), dtype=torch.uint8, device="cuda")
+    asv.markov_pick(B, rows, vocab, chains, P0, W1, W2c, vocab, rank, pick, flag, ws)
+    torch.cuda.synchronize()
+    return pick.cpu().numpy(), flag.cpu().numpy()
+
+
+def _markov_ref(base, chains, prev0, w1, w2, fill_pick=-7, fill_flag=9):
+    rows = base.shape[0]
+    pick = np.full(rows, fill_pick, dtype=np.int32)
+    flag = np.full(rows, fill_flag, dtype=np.uint8)
+    omarkov.markov_pick(base, chains, prev0, w1, w2, pick, flag)
+    return pick, flag
+
+
+def _check_markov(base, chains, prev0, w1, w2):
+    print(f"markov case: vocab {base.shape[1]} rank {w1.shape[1]} chains {chains}", flush=True)
+    gp, gf = _markov_gpu(base, chains, prev0, w1, w2)
+    rp, rf = _markov_ref(base, chains, prev0, w1, w2)
+    assert np.array_equal(gp, rp), (gp, rp)
+    assert np.array_equal(gf, rf), (gf, rf)
+    return gp, gf
+
+
+def test_markov_pack_is_the_chunk_major_layout():
+    rng = np.random.default_rng(11)
+    for vocab, rank in [(1, 8), (1000, 24), (4099, 256)]:
+        w2 = _bf16(rng, (vocab, rank))
+        W2 = _dev(w2.view(np.int16), torch.int16)
+        W2c = torch.empty_like(W2)
+        asv.markov_pack_w2(W2, vocab, rank, W2c)
+        torch.cuda.synchronize()
+        want = w2.reshape(vocab, rank // 8, 8).transpose(1, 0, 2).reshape(-1)
+        assert np.array_equal(W2c.cpu().numpy().view(np.uint16).reshape(-1), want)
+
+
+def test_markov_full_shape_parity():
+    """vocabulary 128,000, rank 256: three chains of depths 3, 2, 1."""
+    rng = np.random.default_rng(12)
+    vocab, rank = 128000, 256
+    w1, w2 = _bf16(rng, (vocab, rank), 0.3), _bf16(rng, (vocab, rank), 0.3)
+    base = _bf16(rng, (6, vocab), 3.0)
+    _check_markov(base, [(0, 3), (3, 2), (5, 1)], [17, 127999, 5000], w1, w2)
+
+
+@pytest.mark.parametrize("vocab,rank,chains", [
+    (1, 8, [(0, 2)]),
+    (7, 16, [(0, 3), (3, 1)]),
+    (255, 64, [(1, 2), (4, 3)]),
+    (256, 8, [(0, 1)]),
+    (257, 256, [(0, 2), (2, 2), (4, 2), (6, 2), (8, 2)]),          # a partial group of four
+    (1000, 24, [(i, 1) for i in range(32)]),                          # the most chains
+    (4099, 136, [(0, 9), (9, 9), (18, 9)]),                           # the drafter's depth
+    (3000, 256, [(0, 16)]),                                           # the longest chain
+])
+def test_markov_ragged_parity(vocab, rank, chains):
+    rng = np.random.default_rng(vocab * 7 + rank)
+    rows = max(r + d for r, d in chains) + 1
+    w1, w2 = _bf16(rng, (vocab, rank), 0.5), _bf16(rng, (vocab, rank), 0.5)
+    base = _bf16(rng, (rows, vocab), 2.0)
+    prev0 = rng.integers(0, vocab, len(chains))
+    gp, gf = _check_markov(base, chains, prev0, w1, w2)
+    assert gp[-1] == -7 and gf[-1] == 9                               # a row in no chain
+
+
+def test_markov_planted_nonfinite_and_invalid_tokens():
+    rng = np.random.default_rng(13)
+    vocab, rank = 5000, 64
+    w1, w2 = _bf16(rng, (vocab, rank), 0.5), _bf16(rng, (vocab, rank), 0.5)
+    w2[4500, 5] = POS_INF                               # token 4500's dot is +-Inf or NaN
+    base = _bf16(rng, (10, vocab), 2.0)
+    base[0, 77] = QNAN
+    base[1, 4000] = POS_INF                             # picked, flagged
+    base[2, :] = NEG_INF                                # every score -Inf (or NaN at 321)
+    base[3, :] = QNAN                                   # no real score: pick 0
+    chains = [(0, 4), (4, 2), (6, 2), (8, 2)]
+    prev0 = [3, -1, vocab, 2**31 - 1]                   # three invalid first tokens
+    gp, gf = _check_markov(base, chains, prev0, w1, w2)
+    assert gf[[0, 1, 3, 4, 6, 8]].tolist() == [1] * 6
+    assert gp[1] == 4000 and gp[3] == 0
+
+
+def test_markov_subnormal_products():
+    """Weights near 2^-64: the products lie near or below float32's smallest
+    normal 2^-126, so a flush to zero anywhere would change the sums, while
+    the sums (near 2^-125) keep enough bf16 steps to tell scores apart."""
+    rng = np.random.default_rng(14)
+    vocab, rank = 2048, 64
+    tiny = 2.0 ** -64
+    w1, w2 = _bf16(rng, (vocab, rank), tiny), _bf16(rng, (vocab, rank), tiny)
+    base = np.zeros((4, vocab), dtype=np.uint16)
+    _check_markov(base, [(0, 4)], [9], w1, w2)
+
+
+def test_markov_ties_go_to_the_lowest_token():
+    vocab, rank = 3000, 8
+    w1 = np.zeros((vocab, rank), dtype=np.uint16)
+    w2 = np.zeros((vocab, rank), dtype=np.uint16)
+    base = np.zeros((2, vocab), dtype=np.uint16)
+    for t in (2999, 1700, 300, 257):                    # equal maxima across blocks
+        base[0, t] = 0x4000                             # 2.0
+    base[1, :] = 0x8000                                 # -0 everywhere: ties with +0
+    base[1, 2500] = 0x0000
+    gp, gf = _check_markov(base, [(0, 2)], [1], w1, w2)
+    assert gp.tolist() == [257, 0] and gf.tolist() == [0, 0]
