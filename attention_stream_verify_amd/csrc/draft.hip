@@ -4,7 +4,7 @@
 // copies each window's drafts from the drafter's picks into the verify's
 // ids, every pick exactly or 0 past the vocabulary, and sets a flag that the
 // verify reads before any cache commit when a pick is NaN, Inf or invalid.
-// The rule per entry is written out in include/asv.h.
+// The rule per entry is written out in include/asv_draft.h.
 //
 // One 256-thread block per stream: threads stride over the stream's span,
 // and a block-wide OR of "this entry failed" becomes the stream's flag. The
@@ -13,6 +13,7 @@
 // stream and is not written.
 
 #include "device.h"
+#include "asv_draft.h"
 
 namespace asv {
 namespace {

@@ -8,7 +8,7 @@
 // bf16(base + bf16(W2 . W1[prev])), at rows x vocabulary x rank
 // 1 x 128,000 x 256; the config admission caps the rank at 256. The exact
 // arithmetic (float32 dot, k ascending, one rounding per term) is written
-// out in include/asv.h.
+// out in include/asv_draft.h.
 //
 // One step is two launches, no atomics: every chain's row at depth j is
 // scored by one scan launch and folded by a one-block launch, which writes
@@ -31,6 +31,7 @@
 #include <utility>
 
 #include "device.h"
+#include "asv_draft.h"
 
 namespace asv {
 namespace {
@@ -201,14 +202,23 @@ __global__ __launch_bounds__(kThreads) void markov_fold(Step st, int nblocks, co
     uint32_t bk = 0;
     uint32_t bt = UINT_MAX;
     bool bad = false;
-    for (int b = lane; b < nblocks; b += 64) {
-      const int4 e = gload(part + int64_t(b) * kMaxChains + ci);
-      const uint32_t k = uint32_t(e.x), t = uint32_t(e.y);
-      if (k > bk || (k == bk && k != 0 && t < bt)) {
-        bk = k;
-        bt = t;
+    // eight records in flight a lane (the loads first, then the compares)
+    for (int b0 = 0; b0 < nblocks; b0 += 64 * 8) {
+      int4 e[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int b = b0 + u * 64 + lane;
+        e[u] = b < nblocks ? gload(part + int64_t(b) * kMaxChains + ci) : make_int4(0, 0, 0, 0);
       }
-      bad |= e.z != 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t k = uint32_t(e[u].x), t = uint32_t(e[u].y);
+        if (k > bk || (k == bk && k != 0 && t < bt)) {
+          bk = k;
+          bt = t;
+        }
+        bad |= e[u].z != 0;
+      }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
