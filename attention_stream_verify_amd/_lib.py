@@ -35,8 +35,10 @@ SYMBOLS = [
     "asv_table_upload",
     "asv_shared_conv", "asv_shared_attn", "asv_attn_merge", "asv_row_argmax_workspace",
     "asv_row_argmax", "asv_draft_ids", "asv_markov_workspace", "asv_markov_pick",
-    "asv_markov_pack_w2",
+    "asv_markov_pack_w2", "asv_shared_qk",
 ]
+
+QKV_WIDTH = 3072
 
 MARKOV_MAX_CHAINS = 32
 MARKOV_MAX_DEPTH = 16
@@ -119,6 +121,9 @@ def lib():
         L.asv_markov_pick.restype = ctypes.c_int
         L.asv_markov_pick.argtypes = [vp, i64, i64, ctypes.POINTER(MarkovChain), i32, vp, vp, vp,
                                       i64, i32, vp, vp, vp, sz, vp]
+        L.asv_shared_qk.restype = ctypes.c_int
+        L.asv_shared_qk.argtypes = [ctypes.POINTER(TableInfo), vp, i32, vp, vp, vp, ctypes.c_double,
+                                    ctypes.c_double, vp, vp]
         L.asv_markov_pack_w2.restype = ctypes.c_int
         L.asv_markov_pack_w2.argtypes = [vp, i64, i32, vp, vp]
         if L.asv_abi_version() != ABI_VERSION:
@@ -307,3 +312,11 @@ def markov_pick(base, rows, row_stride, chains, prev0, w1, w2c, vocab, rank, pic
                                  _addr(w1), _addr(w2c), int(vocab), int(rank), _addr(pick),
                                  _addr(flag), _addr(workspace), nbytes, _stream(stream)),
            "asv_markov_pick")
+
+
+def shared_qk(info, dev_blob, layer, qkv, q_gain, k_gain, theta, eps, q_out, stream=None):
+    """qk stage of attention layer `layer`: q to q_out, k and v into the caches
+    the table names."""
+    _check(lib().asv_shared_qk(ctypes.byref(info), _addr(dev_blob), int(layer), _addr(qkv), _addr(q_gain),
+                               _addr(k_gain), float(theta), float(eps), _addr(q_out), _stream(stream)),
+           "asv_shared_qk")

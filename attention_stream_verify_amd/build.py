@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libasv.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-HIP_SOURCES = ["argmax.hip", "conv.hip", "attn.hip", "merge.hip", "draft.hip", "markov.hip", "upload.hip"]
+HIP_SOURCES = ["argmax.hip", "conv.hip", "attn.hip", "merge.hip", "draft.hip", "markov.hip", "qk.hip", "upload.hip"]
 CXX_SOURCES = ["table.cpp"]
 
 HIPCC_FLAGS = [

@@ -36,6 +36,7 @@ class RoundBuffers:
         self.partials = torch.empty(_lib.partial_floats(info), dtype=torch.float32, device=self.device)
         self.y = torch.empty((R, _lib.HIDDEN), dtype=torch.int16, device=self.device)
         self.o = torch.empty((R, _lib.Q_HEADS, _lib.HEAD_DIM), dtype=torch.int16, device=self.device)
+        self.q = torch.empty((R, _lib.Q_HEADS, _lib.HEAD_DIM), dtype=torch.int16, device=self.device)
         self.pick = torch.empty(R, dtype=torch.int32, device=self.device)
         self.flag = torch.empty(R, dtype=torch.uint8, device=self.device)
         self.vocab = vocab
@@ -56,6 +57,12 @@ class RoundBuffers:
 
     def conv(self, layer, x, w, y=None):
         _lib.shared_conv(self.info, self.blob, layer, x, w, self.y if y is None else y)
+
+    def qk(self, layer, qkv, q_gain, k_gain, theta, eps, q_out=None):
+        """q and k head norm + RoPE into q_out (default self.q); k and v
+        appended to the layer's caches."""
+        _lib.shared_qk(self.info, self.blob, layer, qkv, q_gain, k_gain, theta, eps,
+                       self.q if q_out is None else q_out)
 
     def attn(self, layer, q):
         _lib.shared_attn(self.info, self.blob, layer, q, self.partials)

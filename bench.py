@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--config", type=int, default=3, choices=[0, 1, 2, 3, 4])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-markov", action="store_true", help="skip the Markov-head timing leg")
+    p.add_argument("--with-qk", action="store_true",
+                   help="run the qk stage before every attention layer inside the timed round")
     p.add_argument("--block", action="store_true",
                    help="attention through a block table: every row sees all of its stream's keys")
     p.add_argument("--seed", type=int, default=None)
@@ -250,6 +252,9 @@ def main():
         e.record()
         return e
 
+    qkv, gq, gk = workloads.qk_inputs(R, seed=rnd.seed + 7, device=dev)
+    qk_bytes = R * (2 * 3072 + 2 * 2048 + 2 * 512 + 2 * 512) + 2 * 128   # qkv in; q, k, v out; gains
+
     def step(ev=None, split=False):
         """One round. With ev, records events on torch's current stream (the
         stream the library launches on): round start, then per attention
@@ -264,9 +269,11 @@ def main():
                 X, W, _ = rnd.conv[i]
                 rb.conv(i, X, W)
             else:
+                if args.with_qk:
+                    rb.qk(i, qkv, gq, gk, workloads.ROPE_THETA, workloads.NORM_EPS)
                 if ev is not None:
                     ev[-1].append(event())
-                rb.attn(i, rnd.attn[i][0])
+                rb.attn(i, rb.q if args.with_qk else rnd.attn[i][0])
                 if ev is not None and split:
                     ev[-1].append(event())
                 rb.merge()
@@ -304,17 +311,35 @@ def main():
     def pct(xs, q):
         return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
 
-    # draft-id gather over the round's picks, timed on its own (a few us)
+    # draft-id gather over the round's picks, queued behind an attention
+    # launch like the qk leg below, so the events time the kernels
     rb.draft()
+    rb.attn(0, rnd.attn[0][0])
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     d0.record()
-    for _ in range(100):
+    for _ in range(16):
         rb.draft()
     d1.record()
     torch.cuda.synchronize()
-    draft_us = d0.elapsed_time(d1) * 1e3 / 100
+    draft_us = d0.elapsed_time(d1) * 1e3 / 16
 
     markov = None if args.no_markov else markov_leg(torch, asv, dev, rnd.seed)
+
+    # The qk stage alone: its launches are queued behind an attention launch
+    # (which runs far longer than the host needs to enqueue them), so the GPU
+    # runs them back to back and the events time the kernels, not the
+    # Python calls. One launch per attention layer, three passes.
+    qk_us = []
+    for _ in range(3):
+        rb.attn(0, rnd.attn[0][0])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(rnd.n_attn):
+            rb.qk(i, qkv, gq, gk, workloads.ROPE_THETA, workloads.NORM_EPS)
+        b.record()
+        torch.cuda.synchronize()
+        qk_us.append(a.elapsed_time(b) * 1e3 / rnd.n_attn)
+    qk_avg = sorted(qk_us)[1]
 
     # host table build, timed on its own (pure host code, no HIP calls)
     from attention_stream_verify_amd import _lib
@@ -323,7 +348,9 @@ def main():
                                      [layer[2] for layer in rnd.attn], full=args.block)
 
     line = {
-        "metric": "verify rows/sec per shared round (conv+attn+argmax); attn HBM GB/s vs peak",
+        "metric": ("verify rows/sec per shared round (conv+qk+attn+argmax); attn HBM GB/s vs peak"
+                   if args.with_qk else
+                   "verify rows/sec per shared round (conv+attn+argmax); attn HBM GB/s vs peak"),
         "value": R / (ms_step * 1e-3),
         "unit": "rows/s",
         "n_gpus": 1,
@@ -337,7 +364,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": WORKLOAD_NAMES[args.config] + (", block (non-causal) attention"
-                                                        if args.block else ""),
+                                                        if args.block else "")
+                        + (", qk stage before every attention layer" if args.with_qk else ""),
             "streams": S,
             "rows": R,
             "sum_keys": sum_keys,
@@ -369,6 +397,8 @@ def main():
         "table_build_host_us": build_us,
         "draft_ids_us": draft_us,
         "markov": markov,
+        "qk": {"avg_launch_us": qk_avg, "bytes_per_launch": qk_bytes,
+               "achieved_gbs": qk_bytes / (qk_avg * 1e-6) / 1e9, "in_round": bool(args.with_qk)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

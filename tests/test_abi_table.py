@@ -212,3 +212,22 @@ def test_markov_refusals_on_the_host():
     assert call(chains=[]) == 0                                   # nothing to do, no launch
     assert asv.lib().asv_markov_pack_w2(A, 1000, 12, A * 3, 0) == -3
     assert asv.lib().asv_markov_pack_w2(A, 1000, 64, A + 64, 0) == -1   # overlapping
+
+
+def test_qk_refusals_on_the_host():
+    """theta must be a finite number > 0 (the pages' admission fix), eps
+    finite and >= 0; no launch happens for a refused call."""
+    streams = [(2, 64, 64)]
+    k = [[1 << 20]]
+    v = [[1 << 21]]
+    info, blob = asv.seg_table_build(streams, [], k, v)
+    A = 1 << 24
+    L = asv.lib()
+    def call(theta=1e6, eps=1e-5, layer=0, qkv=A, q_out=A * 2):
+        return L.asv_shared_qk(ctypes.byref(info), A * 3, layer, qkv, A * 4, A * 5, theta, eps, q_out, 0)
+    for bad in (float("inf"), float("nan"), 0.0, -1.0, 1e400):
+        assert call(theta=bad) == -2
+    assert call(eps=-1e-9) == -2 and call(eps=float("nan")) == -2
+    assert call(layer=1) == -2 and call(layer=-1) == -2
+    assert call(qkv=A + 8) == -1 and call(qkv=None) == -1
+    assert call(q_out=A) == -1                                  # q_out overlaps qkv

@@ -153,6 +153,24 @@ def attn_layer(streams, g, device):
     return Q, ks, vs
 
 
+# qk stage constants: the pages give neither; these are stand-ins of the
+# usual size for this model family.
+ROPE_THETA = 1.0e6
+NORM_EPS = 1.0e-5
+
+
+def qk_inputs(R, seed, device):
+    """One attention layer's qk-stage inputs: the rows' qkv projections
+    ~ N(0, 1) and the q and k norm gains ~ 1 + N(0, 0.1^2), as bf16 bits."""
+    g = _gen(device, seed)
+    qkv = _bf16_normal((R, (N_Q + 2 * N_KV) * D), g, device)
+    gains = []
+    for _ in range(2):
+        x = 1.0 + 0.1 * torch.randn((D,), generator=g, device=device, dtype=torch.float32)
+        gains.append(x.to(torch.bfloat16).view(torch.int16))
+    return qkv, gains[0], gains[1]
+
+
 def logits_for(config, R, g, device, vocab=VOCAB):
     """bf16 logits ~ N(0, 3) with the workload's planted ties and nonfinite rows.
 
