@@ -168,6 +168,16 @@ def test_markov_ragged_parity(vocab, rank, chains):
     assert gp[-1] == -7 and gf[-1] == 9                               # a row in no chain
 
 
+def test_markov_large_vocabulary():
+    """2,344 scan blocks a depth (vocab 600,000 at rank 8): the fold reads
+    its records in several rounds of eight a lane."""
+    rng = np.random.default_rng(15)
+    vocab, rank = 600000, 8
+    w1, w2 = _bf16(rng, (vocab, rank), 0.5), _bf16(rng, (vocab, rank), 0.5)
+    base = _bf16(rng, (4, vocab), 2.0)
+    _check_markov(base, [(0, 3)], [123456], w1, w2)
+
+
 def test_markov_planted_nonfinite_and_invalid_tokens():
     rng = np.random.default_rng(13)
     vocab, rank = 5000, 64
