@@ -16,12 +16,26 @@
 
 namespace {
 
-int32_t split_keys_for(int32_t rows) {
+// Split plan of one stream, from its own rows and keys only (so a shared
+// round gives the same bits as each stream alone): the keys are cut into
+// n = ceil(keys / cap) equal splits, each rounded up to a multiple of 32
+// keys (S <= cap, and ceil(keys / S) == n). Few short windows make many
+// small splits; 16-row tiles take splits of up to 7,168 keys, which at
+// 131,072-key contexts puts one tile's 8 heads x 19 splits, and four such
+// streams' 496 work items, on the 512 blocks the device holds at once.
+int32_t split_cap(int32_t rows) {
   const int32_t wt = rows < ASV_TILE_ROWS ? rows : ASV_TILE_ROWS;
   if (wt <= 2) return 512;
   if (wt <= 4) return 1024;
   if (wt <= 8) return 2048;
-  return 4096;
+  return 7168;
+}
+
+int32_t split_keys_for(int32_t rows, int32_t keys) {
+  const int32_t cap = split_cap(rows);
+  const int32_t n = (keys + cap - 1) / cap;
+  const int32_t s = (keys + n - 1) / n;
+  return (s + 31) / 32 * 32;
 }
 
 int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
@@ -120,7 +134,7 @@ int build_table(const asv_stream_desc* streams, int32_t n_streams, const void* c
     g.rows = d.rows;
     g.keys = d.key_count;
     g.cap = d.kv_capacity;
-    g.split_keys = split_keys_for(d.rows);
+    g.split_keys = split_keys_for(d.rows, d.key_count);
     g.nsplit = (d.key_count + g.split_keys - 1) / g.split_keys;
     g.poff = poff;
     poff += int64_t(g.nsplit) * d.rows * ASV_Q_HEADS;

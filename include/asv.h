@@ -84,8 +84,10 @@ typedef struct {      /* one per stream, caller order                     */
   int32_t rows;
   int32_t keys;
   int32_t cap;
-  int32_t split_keys; /* keys per split: 512, 1024, 2048 or 4096 by the
-                         stream's rows (<= 2, <= 4, <= 8, more)           */
+  int32_t split_keys; /* keys per split: the keys cut into ceil(keys/C)
+                         equal splits rounded up to 32, C = 512, 1024,
+                         2048 or 7168 by the stream's rows (<= 2, <= 4,
+                         <= 8, more)                                      */
   int32_t nsplit;     /* ceil(keys / split_keys)                          */
   int64_t poff;       /* first partial record of the stream               */
 } asv_seg;

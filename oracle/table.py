@@ -15,10 +15,12 @@ definitions (the readings are listed in the design notes):
   pos = r - off_s, and sees n_r = K_s - w_s + pos + 1 keys (causal inside the
   window);
 * tiles: runs of at most 16 consecutive rows, never across streams;
-* split plan: the split size depends only on the stream's own rows (so a
-  shared round gives the same bits as each stream alone): with
-  wt = min(w_s, 16), S_s = 512 (wt <= 2), 1024 (wt <= 4), 2048 (wt <= 8),
-  4096 (otherwise); nsplit_s = ceil(K_s / S_s);
+* split plan: the split size depends only on the stream's own rows and
+  keys (so a shared round gives the same bits as each stream alone): with
+  wt = min(w_s, 16), the cap C_s = 512 (wt <= 2), 1024 (wt <= 4),
+  2048 (wt <= 8), 7168 (otherwise); the keys are cut into
+  n_s = ceil(K_s / C_s) equal splits, S_s = ceil(K_s / n_s) rounded up to a
+  multiple of 32 (so S_s <= C_s and nsplit_s = ceil(K_s / S_s) = n_s);
 * partial records: stream s owns records [poff_s, poff_s + nsplit_s*w_s*32),
   poff being the exclusive prefix sum of nsplit_s*w_s*32; the record of
   (row r, q head h, split t) is poff_s + (t*w_s + pos_r)*32 + h;
@@ -45,8 +47,8 @@ MAX_ROWS = 2048
 MAX_KEYS = 131072
 
 
-def split_keys(rows):
-    """Split size S_s for a stream of ``rows`` window rows."""
+def split_cap(rows):
+    """Largest split C_s for a stream of ``rows`` window rows."""
     wt = min(int(rows), TILE_ROWS)
     if wt <= 2:
         return 512
@@ -54,7 +56,16 @@ def split_keys(rows):
         return 1024
     if wt <= 8:
         return 2048
-    return 4096
+    return 7168
+
+
+def split_keys(rows, keys):
+    """Split size S_s: K_s keys cut into ceil(K_s / C_s) equal splits, each
+    rounded up to a multiple of 32 keys."""
+    cap = split_cap(rows)
+    n = -(-int(keys) // cap)
+    s = -(-int(keys) // n)
+    return -(-s // 32) * 32
 
 
 @dataclass
@@ -136,7 +147,7 @@ def build(streams, full=False):
             p += n
     tiles = np.array(tiles, dtype=np.int64).reshape(-1, 4)
 
-    split = np.array([split_keys(w) for w in rows], dtype=np.int64)
+    split = np.array([split_keys(rows[s], keys[s]) for s in range(S)], dtype=np.int64)
     nsplit = np.array([-(-keys[s] // split[s]) for s in range(S)], dtype=np.int64)
     poff = np.zeros(S, dtype=np.int64)
     acc = 0

@@ -105,9 +105,27 @@ def test_table_invariants_random(streams):
 
 
 def test_table_split_plan_by_window():
-    # the split size depends only on the stream's own rows
-    assert [table.split_keys(w) for w in (1, 2, 3, 4, 5, 8, 9, 16, 17, 512)] == \
-        [512, 512, 1024, 1024, 2048, 2048, 4096, 4096, 4096, 4096]
+    # the cap depends only on the stream's own rows
+    assert [table.split_cap(w) for w in (1, 2, 3, 4, 5, 8, 9, 16, 17, 512)] == \
+        [512, 512, 1024, 1024, 2048, 2048, 7168, 7168, 7168, 7168]
+    # equal splits, by hand: 65,536 / ceil(65,536 / 7,168) = 6,553.6 -> 6,560;
+    # 98,304 / 14 = 7,021.7 -> 7,040; 131,072 / 19 = 6,898.5 -> 6,912;
+    # 1,000 / 2 = 500 -> 512; 100 / 1 -> 128; 4,096 / 8 = 512
+    assert [table.split_keys(w, k) for (w, k) in
+            ((16, 65536), (16, 98304), (16, 131072), (1, 1000), (3, 100), (1, 4096))] == \
+        [6560, 7040, 6912, 512, 128, 512]
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.integers(1, 16), st.integers(1, 131072))
+def test_table_split_plan_properties(rows, keys):
+    cap = table.split_cap(rows)
+    S = table.split_keys(rows, keys)
+    n = -(-keys // S)
+    assert S % 32 == 0 and S <= cap
+    assert n == -(-keys // cap)                  # as many splits as the cap forces
+    assert (n - 1) * S < keys <= n * S
+    assert n * S - keys < 32 * n + S - (keys // n)  # nearly equal: every split but the last is full
 
 
 @pytest.mark.parametrize("rows,expect", [
@@ -115,8 +133,8 @@ def test_table_split_plan_by_window():
     ([(1, 4096, 4096)], 256),
     # 32 rows as 32 one-row streams of 1,000 keys: 2 splits each -> 32 * 2 * 32
     ([(1, 1000, 1024)] * 32, 2048),
-    # 2,048 rows as 128 streams of 16 rows and 131,072 keys: 32 splits each
-    ([(16, 131072, 131072)] * 128, 128 * 16 * 32 * 32),
+    # 2,048 rows as 128 streams of 16 rows and 131,072 keys: 19 splits each
+    ([(16, 131072, 131072)] * 128, 128 * 16 * 32 * 19),
 ])
 def test_table_partial_counts_at_1_32_2048_rows(rows, expect):
     t = table.build(rows)
