@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--config", type=int, default=3, choices=[0, 1, 2, 3, 4])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-markov", action="store_true", help="skip the Markov-head timing leg")
+    p.add_argument("--eager", action="store_true",
+                   help="time the rounds as eager launches (default: replays of one captured HIP graph)")
     p.add_argument("--with-qk", action="store_true",
                    help="run the qk stage before every attention layer inside the timed round")
     p.add_argument("--block", action="store_true",
@@ -311,6 +313,26 @@ def main():
     def pct(xs, q):
         return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
 
+    # The round as one captured HIP graph (the table upload and every
+    # launch, on the capture stream), replayed W times untimed and K times
+    # timed: the same work with the host's per-launch cost taken out. The
+    # eager rounds above stay the source of the per-kernel event timings.
+    eager_ms_step = ms_step
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_step = g0.elapsed_time(g1) / args.steps
+
     # draft-id gather over the round's picks, queued behind an attention
     # launch like the qk leg below, so the events time the kernels
     rb.draft()
@@ -385,6 +407,8 @@ def main():
             "bytes_per_launch": attn_bytes,
             "avg_launch_us": attn_avg_ms * 1e3,
         },
+        "launch": "eager" if args.eager else "hip graph of one round",
+        "eager_ms_per_step": eager_ms_step,
         "round_ms": {"median": round_ms[len(round_ms) // 2], "p10": pct(round_ms, 0.1),
                      "p90": pct(round_ms, 0.9)},
         "attn_merge": {
