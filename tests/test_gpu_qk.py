@@ -95,3 +95,42 @@ def test_qk_then_attention_reads_the_appended_keys():
     t = otable.build(rnd.streams)
     ref = oattn.attention(t, _u16(rb.q), [_u16(k) for k in K], [_u16(workloads.v_logical(v)) for v in V])
     assert np.abs(o - ref).max() <= 2e-2
+
+
+@pytest.mark.parametrize("streams", [
+    [(16, 16, 32), (1, 1, 32), (3, 131072, 131072)],   # window = cache (positions from 0), one key, the last position
+    [(7, 40, 64)] * 5 + [(16, 4096, 4096)],
+])
+def test_qk_edge_streams(streams):
+    print(f"qk edge: {streams}", flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    K, V = [], []
+    for (_, keys, cap) in streams:
+        k, v = workloads.kv_cache(keys, cap, g, "cuda")
+        K.append(k)
+        V.append(v)
+    R = sum(w for w, _, _ in streams)
+    qkv, gq, gk = workloads.qk_inputs(R, seed=5, device="cuda")
+    K0 = [_u16(k) for k in K]
+    V0 = [_u16(workloads.v_logical(v)) for v in V]
+    rb = asv.RoundBuffers(streams, [], [K], [V], device="cuda")
+    rb.upload()
+    rb.qk(0, qkv, gq, gk, workloads.ROPE_THETA, workloads.NORM_EPS)
+    torch.cuda.synchronize()
+    Qg = _u16(rb.q)
+    K1 = [_u16(k) for k in K]
+    V1 = [_u16(workloads.v_logical(v)) for v in V]
+    qkv_h = _u16(qkv)
+    _, _, Vn, st, pos = oqk.qk_rows(streams, qkv_h, _u16(gq), _u16(gk), workloads.ROPE_THETA, workloads.NORM_EPS)
+    gqf, gkf = obf16.to_f64(_u16(gq)), obf16.to_f64(_u16(gk))
+    for r in range(R):
+        row = obf16.to_f64(qkv_h[r])
+        _check_heads(Qg[r], row[:2048].reshape(32, 64), gqf, pos[r], f"q row {r}")
+        _check_heads(K1[st[r]][:, pos[r]], row[2048:2560].reshape(8, 64), gkf, pos[r], f"k row {r}")
+        assert np.array_equal(V1[st[r]][:, pos[r]], Vn[r])
+    for s, (w, keys, _cap) in enumerate(streams):
+        keep = np.ones(K0[s].shape[1], dtype=bool)
+        keep[keys - w:keys] = False
+        assert np.array_equal(K1[s][:, keep], K0[s][:, keep]) and np.array_equal(V1[s][:, keep], V0[s][:, keep])
+    assert pos.max() == max(k - 1 for _, k, _ in streams)
