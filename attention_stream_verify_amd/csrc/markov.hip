@@ -10,6 +10,26 @@
 // arithmetic (float32 dot, k ascending, one rounding per term) is written
 // out in include/asv_draft.h.
 //
+// A pass of depth D is D scan launches and one fold launch, no atomics.
+// The scan of depth j scores every chain's row at that depth and leaves,
+// per chain, one 4-byte record a block (its best order key and lane, and a
+// nonfinite bit). The scan of depth j + 1 starts by folding those records
+// in every block (each block needs the previous tokens; the records are a
+// few KB and are read from cache, while the block's W2 loads, issued right
+// after them, stream from HBM), and its block 0 writes depth j's picks and
+// flags. A last one-block launch folds the deepest depth. Depths alternate
+// between the two halves of the workspace, so no block overwrites records
+// that another block of the same launch still folds.
+//
+// Scan: one thread per token v, 256 tokens a block. W2 is stored
+// chunk-major ([rank/8][vocab][8]: the 8 coefficients k = 8c..8c+7 of token
+// v at chunk c), so one 16-byte load per lane per chunk is a contiguous 1 KB
+// per wave; a lane issues all rank/8 loads of its token first (up to 128
+// VGPRs, 32 KB a wave in flight). The chains' W1 rows are the same for the
+// whole block: they are converted to float32 into LDS once, and each
+// multiply-add reads its W1 value by an LDS broadcast. The dot is summed one
+// k at a time in float32 (a fused multiply-add of an exact product), four
+// chains at a time so that each converted W2 value serves four chains.
 // One step is two launches, no atomics: every chain's row at depth j is
 // scored by one scan launch and folded by a one-block launch, which writes
 // the picks that the next step's scan reads as previous tokens.
@@ -41,17 +61,19 @@ constexpr int kMaxChains = ASV_MARKOV_MAX_CHAINS;
 constexpr int kMaxChunks = ASV_MARKOV_MAX_RANK / 8;
 constexpr int kGroup = 4;  // chains scored together
 
-// The chains' rows at one depth: row[i] is chain i's logits / pick row;
-// prev[i] >= 0 names the pick row holding its previous token, prev[i] < 0
-// names prev0[-1 - prev[i]] (the first row's given token).
+// One depth: the chains scored at it, and the chains of the depth before,
+// whose block records the launch folds first.
 struct Step {
-  int32_t n;
-  int32_t row[kMaxChains];
-  int32_t prev[kMaxChains];
+  int32_t n;                  // chains scored at this depth
+  int32_t row[kMaxChains];    // chain i's logits / pick row
+  int32_t src[kMaxChains];    // its previous token: src >= 0, the fold result of
+                              // chain src of the depth before; src < 0, prev0[-1 - src]
+  int32_t nprev;              // chains of the depth before (0 at the first depth)
+  int32_t prow[kMaxChains];   // their pick rows
 };
 
 // Order key of a non-NaN bf16 pattern: larger key = larger value; -0 and +0
-// share a key.
+// share a key. Every non-NaN pattern has a key >= 0x7F.
 __device__ __forceinline__ uint32_t order_key(uint32_t b) {
   b = (b == 0x8000u) ? 0u : b;
   return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
@@ -68,6 +90,62 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
   return x;
 }
 
+// A block record: bits 8..23 the order key of the block's largest score and
+// bits 0..7 255 - its lane (so the lower token wins a tie inside the block),
+// both 0 when every score of the block is NaN; bit 31 the nonfinite flag.
+constexpr uint32_t kRecKey = 0x00FFFFFFu;
+constexpr uint32_t kRecBad = 0x80000000u;
+
+// Fold one chain's records (nblocks of them) in one wave: the largest order
+// key, then the lowest token. Loads are issued by fold_load (eight a lane in
+// flight) and consumed by fold_use, so a caller can put other loads after
+// them.
+struct FoldAcc {
+  uint32_t hi, lo;  // (order key, ~token) of the best so far, (0, 0) for none
+  bool bad;
+};
+
+__device__ __forceinline__ void fold_use(FoldAcc& a, const uint32_t (&e)[8], int b0, int lane) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t key = e[u] & kRecKey;
+    a.bad |= (e[u] & kRecBad) != 0u;
+    if (key != 0u) {
+      const uint32_t b = uint32_t(b0 + u * 64 + lane);
+      const uint32_t tok = b * kThreads + (kThreads - 1 - (key & 0xFFu));
+      const uint32_t hi = key >> 8, lo = ~tok;
+      if (hi > a.hi || (hi == a.hi && lo > a.lo)) {
+        a.hi = hi;
+        a.lo = lo;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void fold_load(uint32_t (&e)[8], const uint32_t* __restrict__ rec, int nblocks,
+                                          int b0, int lane) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int b = b0 + u * 64 + lane;
+    e[u] = b < nblocks ? gload(rec + b) : 0u;
+  }
+}
+
+// Wave-wide result of a fold: the token (0 when every score was NaN) and the flag.
+__device__ __forceinline__ void fold_finish(FoldAcc a, uint32_t& tok, bool& bad) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t oh = uint32_t(__shfl_xor(int(a.hi), off));
+    const uint32_t ol = uint32_t(__shfl_xor(int(a.lo), off));
+    if (oh > a.hi || (oh == a.hi && ol > a.lo)) {
+      a.hi = oh;
+      a.lo = ol;
+    }
+  }
+  tok = a.hi != 0u ? ~a.lo : 0u;
+  bad = __any(a.bad);
+}
+
 // NCH = rank / 8, a compile-time count so that every chunk loop is straight
 // code with no per-chunk guard.
 template <int NCH>
@@ -75,81 +153,145 @@ __global__ __launch_bounds__(kThreads, 2) void markov_scan(Step st, const uint16
                                                            int64_t stride, const int32_t* __restrict__ prev0,
                                                            const uint16_t* __restrict__ w1,
                                                            const uint16_t* __restrict__ w2c, int vocab,
-                                                           const int32_t* __restrict__ pick,
-                                                           int4* __restrict__ part) {
+                                                           int nblocks, const uint32_t* __restrict__ prec,
+                                                           uint32_t* __restrict__ rec,
+                                                           int32_t* __restrict__ pick,
+                                                           uint8_t* __restrict__ flag) {
+  constexpr int rank = NCH * 8;
+  __shared__ __attribute__((aligned(16))) float s_w1[kMaxChains][rank];
   __shared__ uint32_t s_key[kThreads / 64][kMaxChains];
   __shared__ uint32_t s_bad[kThreads / 64][kMaxChains];
+  __shared__ int32_t s_ptok[kMaxChains];
+  __shared__ int32_t s_prev[kMaxChains];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int wave = tid >> 6;
   const int v = blockIdx.x * kThreads + tid;
   const bool live = v < vocab;
   const int vc = live ? v : vocab - 1;
-  constexpr int rank = NCH * 8;
 
+  // The depth before: wave w folds its chains w, w + 4, ...; the first
+  // chain's records are requested before the W2 loads, so waiting for them
+  // does not wait for W2.
+  const int nfold = st.nprev;
+  FoldAcc fa{0u, 0u, false};
+  uint32_t fe[8];
+  const bool fold_first = wave < nfold;
+  if (fold_first) fold_load(fe, prec + int64_t(wave) * nblocks, nblocks, 0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // W2 in two halves: the first now, the second after the W1 loads, so
+  // that waiting for W1 waits for the first half only and the first half
+  // is scored while the second streams in (load counts retire in order)
+  constexpr int kHalf = (NCH + 1) / 2;
   u32x4 w[NCH];
-  {
-    const uint16_t* wp = w2c + int64_t(vc) * 8;
-    const int64_t plane = int64_t(vocab) * 8;
+  const uint16_t* wp = w2c + int64_t(vc) * 8;
+  const int64_t plane = int64_t(vocab) * 8;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) w[c] = load16(wp + c * plane);
+  for (int c = 0; c < kHalf; ++c) w[c] = load16(wp + c * plane);
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int ci = wave; ci < nfold; ci += kThreads / 64) {
+    const uint32_t* r = prec + int64_t(ci) * nblocks;
+    if (ci != wave) {
+      fa = FoldAcc{0u, 0u, false};
+      fold_load(fe, r, nblocks, 0, lane);
+    }
+    fold_use(fa, fe, 0, lane);
+    for (int b0 = 64 * 8; b0 < nblocks; b0 += 64 * 8) {
+      fold_load(fe, r, nblocks, b0, lane);
+      fold_use(fa, fe, b0, lane);
+    }
+    uint32_t tok;
+    bool bad;
+    fold_finish(fa, tok, bad);
+    if (lane == 0) {
+      s_ptok[ci] = int32_t(tok);
+      if (blockIdx.x == 0) {
+        gstore(pick + st.prow[ci], int32_t(tok));
+        gstore(flag + st.prow[ci], uint8_t(bad ? 1 : 0));
+      }
+    }
   }
+  __syncthreads();
+
+  // previous tokens, then the chains' W1 rows in float32 (row 0 stands in
+  // for an invalid token: its sum is replaced by +0)
+  if (tid < st.n) {
+    const int src = st.src[tid];
+    s_prev[tid] = src >= 0 ? s_ptok[src] : cload(prev0 + (-1 - src));
+  }
+  __syncthreads();
+  // one 16-byte piece of a W1 row a thread and pass (n * rank / 8 pieces,
+  // at most 1,024: four passes), all requested before the second W2 half
+  constexpr int kPass = (kMaxChains * NCH + kThreads - 1) / kThreads;
+  u32x4 q[kPass];
+#pragma unroll
+  for (int k = 0; k < kPass; ++k) {
+    const int idx = tid + k * kThreads;
+    if (idx < st.n * NCH) {
+      const int ci = idx / NCH;
+      const int p = s_prev[ci];
+      const bool ok = p >= 0 && p < vocab;
+      q[k] = load16(w1 + int64_t(ok ? p : 0) * rank + (idx - ci * NCH) * 8);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = kHalf; c < NCH; ++c) w[c] = load16(wp + c * plane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < kPass; ++k) {
+    const int idx = tid + k * kThreads;
+    if (idx < st.n * NCH) {
+      const int ci = idx / NCH;
+      const int c = idx - ci * NCH;
+      float4 a, b;
+      a.x = bf16_lo(q[k][0]); a.y = bf16_hi(q[k][0]); a.z = bf16_lo(q[k][1]); a.w = bf16_hi(q[k][1]);
+      b.x = bf16_lo(q[k][2]); b.y = bf16_hi(q[k][2]); b.z = bf16_lo(q[k][3]); b.w = bf16_hi(q[k][3]);
+      *reinterpret_cast<float4*>(&s_w1[ci][c * 8]) = a;
+      *reinterpret_cast<float4*>(&s_w1[ci][c * 8 + 4]) = b;
+    }
+  }
+  __syncthreads();
 
   for (int g = 0; g < st.n; g += kGroup) {
     // Keep W2 as raw bf16 pairs between groups (128 VGPRs); converting it
     // once for every group would hold 256 floats and spill.
 #pragma unroll
     for (int c = 0; c < NCH; ++c) asm volatile("" : "+v"(w[c]));
-    const uint16_t* er[kGroup];
     bool ok[kGroup];
     uint32_t bv[kGroup];
+    int cs[kGroup];
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
-      const int ci = min(g + i, st.n - 1);
-      const int src = st.prev[ci];
-      const int p = src >= 0 ? cload(pick + src) : cload(prev0 + (-1 - src));
+      cs[i] = min(g + i, st.n - 1);
+      const int p = s_prev[cs[i]];
       ok[i] = p >= 0 && p < vocab;
-      er[i] = w1 + int64_t(ok[i] ? p : 0) * rank;
-      bv[i] = live ? uint32_t(gload(base + int64_t(st.row[ci]) * stride + v)) : 0u;
+      bv[i] = live ? uint32_t(gload(base + int64_t(st.row[cs[i]]) * stride + v)) : 0u;
     }
 
-    // W1's chunk c + 1 is requested while chunk c is summed (scalar loads,
-    // one chunk ahead: 32 SGPRs a stage); the barrier keeps the scheduler
-    // from pulling every chunk's scalar loads to the front.
     float acc[kGroup] = {0.f, 0.f, 0.f, 0.f};
-    u32x4 e[kGroup];
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) e[i] = cload(reinterpret_cast<const u32x4*>(er[i]));
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      {
-        u32x4 en[kGroup];
-        if (c + 1 < NCH) {
-          // an opaque offset: the loads can be neither merged across chunks
-          // nor hoisted above this chunk
-          int off = (c + 1) * 8;
-          asm volatile("" : "+s"(off));
+      float f[8];
 #pragma unroll
-          for (int i = 0; i < kGroup; ++i) en[i] = cload(reinterpret_cast<const u32x4*>(er[i] + off));
-        }
-        float f[8];
+      for (int k = 0; k < 4; ++k) {
+        f[2 * k] = bf16_lo(w[c][k]);
+        f[2 * k + 1] = bf16_hi(w[c][k]);
+      }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          f[2 * k] = bf16_lo(w[c][k]);
-          f[2 * k + 1] = bf16_hi(w[c][k]);
-        }
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            acc[i] = __builtin_fmaf(f[2 * k], bf16_lo(e[i][k]), acc[i]);
-            acc[i] = __builtin_fmaf(f[2 * k + 1], bf16_hi(e[i][k]), acc[i]);
-          }
-        }
-        if (c + 1 < NCH) {
-#pragma unroll
-          for (int i = 0; i < kGroup; ++i) e[i] = en[i];
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < kGroup; ++i) {
+        const float4 a = *reinterpret_cast<const float4*>(&s_w1[cs[i]][c * 8]);
+        const float4 b = *reinterpret_cast<const float4*>(&s_w1[cs[i]][c * 8 + 4]);
+        acc[i] = __builtin_fmaf(f[0], a.x, acc[i]);
+        acc[i] = __builtin_fmaf(f[1], a.y, acc[i]);
+        acc[i] = __builtin_fmaf(f[2], a.z, acc[i]);
+        acc[i] = __builtin_fmaf(f[3], a.w, acc[i]);
+        acc[i] = __builtin_fmaf(f[4], b.x, acc[i]);
+        acc[i] = __builtin_fmaf(f[5], b.y, acc[i]);
+        acc[i] = __builtin_fmaf(f[6], b.z, acc[i]);
+        acc[i] = __builtin_fmaf(f[7], b.w, acc[i]);
       }
     }
 
@@ -167,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void markov_scan(Step st, const uint16
       uint32_t key = (live && !nan) ? (order_key(s) << 8) | uint32_t(kThreads - 1 - tid) : 0u;
       key = wave_umax(key);
       const bool bad = __any(nonfinite) || !ok[i];
-      if ((tid & 63) == 0 && g + i < st.n) {
+      if (lane == 0 && g + i < st.n) {
         s_key[wave][g + i] = key;
         s_bad[wave][g + i] = bad ? 1u : 0u;
       }
@@ -181,58 +323,30 @@ __global__ __launch_bounds__(kThreads, 2) void markov_scan(Step st, const uint16
       key = s_key[wv][tid] > key ? s_key[wv][tid] : key;
       bad |= s_bad[wv][tid];
     }
-    // (order key, token) of the block's best, or (0, 0) when every score is NaN
-    const int tok = key ? blockIdx.x * kThreads + (kThreads - 1 - int(key & 0xFFu)) : 0;
-    u32x4 rec;
-    rec[0] = key >> 8;
-    rec[1] = uint32_t(tok);
-    rec[2] = bad;
-    rec[3] = 0u;
-    store16(part + int64_t(blockIdx.x) * kMaxChains + tid, rec);
+    gstore(rec + int64_t(tid) * nblocks + blockIdx.x, key | (bad ? kRecBad : 0u));
   }
 }
 
-// One block: wave w folds chains w, w + 4, ...; lanes stride over the scan
-// blocks. Larger order key wins, then the lower token.
-__global__ __launch_bounds__(kThreads) void markov_fold(Step st, int nblocks, const int4* __restrict__ part,
+// The deepest depth's fold, one block: wave w folds chains w, w + 4, ...
+__global__ __launch_bounds__(kThreads) void markov_fold(Step st, int nblocks,
+                                                        const uint32_t* __restrict__ prec,
                                                         int32_t* __restrict__ pick,
                                                         uint8_t* __restrict__ flag) {
   const int lane = threadIdx.x & 63;
-  for (int ci = threadIdx.x >> 6; ci < st.n; ci += kThreads / 64) {
-    uint32_t bk = 0;
-    uint32_t bt = UINT_MAX;
-    bool bad = false;
-    // eight records in flight a lane (the loads first, then the compares)
+  for (int ci = threadIdx.x >> 6; ci < st.nprev; ci += kThreads / 64) {
+    const uint32_t* r = prec + int64_t(ci) * nblocks;
+    FoldAcc fa{0u, 0u, false};
     for (int b0 = 0; b0 < nblocks; b0 += 64 * 8) {
-      int4 e[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int b = b0 + u * 64 + lane;
-        e[u] = b < nblocks ? gload(part + int64_t(b) * kMaxChains + ci) : make_int4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t k = uint32_t(e[u].x), t = uint32_t(e[u].y);
-        if (k > bk || (k == bk && k != 0 && t < bt)) {
-          bk = k;
-          bt = t;
-        }
-        bad |= e[u].z != 0;
-      }
+      uint32_t e[8];
+      fold_load(e, r, nblocks, b0, lane);
+      fold_use(fa, e, b0, lane);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const uint32_t ok = uint32_t(__shfl_xor(int(bk), off));
-      const uint32_t ot = uint32_t(__shfl_xor(int(bt), off));
-      if (ok > bk || (ok == bk && ot < bt)) {
-        bk = ok;
-        bt = ot;
-      }
-    }
-    bad = __any(bad);
+    uint32_t tok;
+    bool bad;
+    fold_finish(fa, tok, bad);
     if (lane == 0) {
-      gstore(pick + st.row[ci], int32_t(bk ? bt : 0u));
-      gstore(flag + st.row[ci], uint8_t(bad ? 1 : 0));
+      gstore(pick + st.prow[ci], int32_t(tok));
+      gstore(flag + st.prow[ci], uint8_t(bad ? 1 : 0));
     }
   }
 }
@@ -250,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void markov_pack(const uint16_t* __restri
 int64_t scan_blocks(int64_t vocab) { return (vocab + kThreads - 1) / kThreads; }
 
 typedef void (*ScanFn)(Step, const uint16_t*, int64_t, const int32_t*, const uint16_t*, const uint16_t*, int,
-                       const int32_t*, int4*);
+                       int, const uint32_t*, uint32_t*, int32_t*, uint8_t*);
 
 template <int... N>
 constexpr auto scan_table(std::integer_sequence<int, N...>) {
@@ -266,7 +380,8 @@ bool rank_ok(int32_t rank) { return rank >= 8 && rank <= ASV_MARKOV_MAX_RANK && 
 
 extern "C" size_t asv_markov_workspace(int64_t vocab) {
   if (vocab < 1 || vocab > (int64_t(1) << 30)) return 0;
-  return size_t(asv::scan_blocks(vocab)) * asv::kMaxChains * sizeof(int4);
+  // two halves (depths alternate), each a record per chain and scan block
+  return 2 * size_t(asv::scan_blocks(vocab)) * asv::kMaxChains * sizeof(uint32_t);
 }
 
 extern "C" int asv_markov_pack_w2(const uint16_t* w2, int64_t vocab, int32_t rank, uint16_t* w2c,
@@ -316,21 +431,35 @@ extern "C" int asv_markov_pick(const uint16_t* base, int64_t rows, int64_t row_s
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int nblocks = int(asv::scan_blocks(vocab));
-  int4* part = static_cast<int4*>(workspace);
+  uint32_t* half[2] = {static_cast<uint32_t*>(workspace),
+                       static_cast<uint32_t*>(workspace) + int64_t(nblocks) * asv::kMaxChains};
+  asv::Step s{};
+  int idx[ASV_MARKOV_MAX_CHAINS];  // chain i's index in the depth before, -1 when absent
   for (int j = 0; j < max_depth; ++j) {
-    asv::Step s{};
+    asv::Step t{};
+    t.nprev = s.n;
+    for (int i = 0; i < s.n; ++i) t.prow[i] = s.row[i];
+    int nidx[ASV_MARKOV_MAX_CHAINS];
     for (int i = 0; i < n_chains; ++i) {
+      nidx[i] = -1;
       if (chains[i].depth <= j) continue;
-      s.row[s.n] = chains[i].row0 + j;
-      s.prev[s.n] = j == 0 ? -1 - i : chains[i].row0 + j - 1;
-      ++s.n;
+      t.row[t.n] = chains[i].row0 + j;
+      t.src[t.n] = j == 0 ? -1 - i : idx[i];
+      nidx[i] = t.n;
+      ++t.n;
     }
-    hipLaunchKernelGGL(asv::scan_for[rank / 8 - 1], dim3(unsigned(nblocks)), dim3(asv::kThreads), 0, st, s,
-                       base, row_stride, prev0, w1, w2c, int(vocab), pick, part);
+    hipLaunchKernelGGL(asv::scan_for[rank / 8 - 1], dim3(unsigned(nblocks)), dim3(asv::kThreads), 0, st, t,
+                       base, row_stride, prev0, w1, w2c, int(vocab), nblocks, half[(j + 1) & 1],
+                       half[j & 1], pick, flag);
     if (hipGetLastError() != hipSuccess) return ASV_E_HIP;
-    hipLaunchKernelGGL(asv::markov_fold, dim3(1), dim3(asv::kThreads), 0, st, s, nblocks, part, pick,
-                       flag);
-    if (hipGetLastError() != hipSuccess) return ASV_E_HIP;
+    s = t;
+    for (int i = 0; i < n_chains; ++i) idx[i] = nidx[i];
   }
+  asv::Step f{};
+  f.nprev = s.n;
+  for (int i = 0; i < s.n; ++i) f.prow[i] = s.row[i];
+  hipLaunchKernelGGL(asv::markov_fold, dim3(1), dim3(asv::kThreads), 0, st, f, nblocks,
+                     half[(max_depth - 1) & 1], pick, flag);
+  if (hipGetLastError() != hipSuccess) return ASV_E_HIP;
   return ASV_OK;
 }

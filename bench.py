@@ -215,7 +215,7 @@ def markov_leg(torch, asv, dev, seed, calls=20):
     depth = 8
     nbytes = depth * vocab * rank * 2 + rows * vocab * 2 + rows * rank * 2
     return {"shape": "4 chains x depth 8, vocab 128,000, rank 256", "avg_call_us": us,
-            "launches_per_call": 2 * depth, "bytes_per_call": nbytes,
+            "launches_per_call": depth + 1, "bytes_per_call": nbytes,
             "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
             "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 

@@ -89,9 +89,12 @@ int asv_draft_ids(const asv_draft_span* spans, int32_t n_streams, const int32_t*
  *              (v, k) at ((k / 8) * vocab + v) * 8 + k % 8 (asv_markov_pack_w2)
  *   pick, flag device, int32 / uint8 [rows]
  *   workspace  device, asv_markov_workspace(vocab) bytes, 16-byte aligned;
- *              one call at a time per workspace
- * Two launches a depth on `stream`; the picks of depth j are read by depth
- * j + 1 on the device, never by the host.
+ *              one call at a time per workspace (two halves of one 4-byte
+ *              record per chain and 256-token block, depths alternating)
+ * One launch a depth plus one on `stream`: the launch of depth j + 1 folds
+ * depth j's block records for its previous tokens (its block 0 writes
+ * depth j's picks and flags), and the last launch folds the deepest depth;
+ * the host never reads a pick.
  * Errors: ASV_E_SHAPE (n_chains > ASV_MARKOV_MAX_CHAINS, a depth outside
  * 1..ASV_MARKOV_MAX_DEPTH, a chain outside [0, rows) or two chains sharing a
  * row, vocab < 1 or > 2^30, row_stride < vocab); ASV_E_UNSUPPORTED (rank not
