@@ -8,7 +8,8 @@
 // non-NaN value picks 0.
 //
 // Two launches, no atomics: each block scans an 8,192-logit chunk of one row
-// with 16-byte coalesced loads (4 KB per block per step) and writes its
+// with 16-byte coalesced loads (4 KB per block per step; a whole chunk's
+// four loads a thread are issued before its compares) and writes its
 // (value, id, flag) to the workspace; a second launch folds each row's
 // chunks. Many blocks per row keep small rounds (10-16 rows) from running on
 // a handful of CUs. The result is exact, so the chunking never changes it.
@@ -48,18 +49,29 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks(const uint16_t* __rest
   float bv = -__builtin_inff();
   int bi = INT_MAX;
   uint32_t bad = 0;
+  auto scan8 = [&](const u32x4& w, int64_t e0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t x = w[k];
+      bad |= ((x & 0x7F80u) == 0x7F80u) | ((x & 0x7F800000u) == 0x7F800000u);
+      take(bf16_lo(x), int(e0) + 2 * k, bv, bi);
+      take(bf16_hi(x), int(e0) + 2 * k + 1, bv, bi);
+    }
+  };
+  if (base + kChunk <= vocab) {
+    // a whole chunk: every load of the thread in flight before any compare
+    u32x4 w[kSteps];
+#pragma unroll
+    for (int it = 0; it < kSteps; ++it)
+      w[it] = load16(p + base + int64_t(it) * (kThreads * 8) + threadIdx.x * 8);
+#pragma unroll
+    for (int it = 0; it < kSteps; ++it) scan8(w[it], base + int64_t(it) * (kThreads * 8) + threadIdx.x * 8);
+  } else {
 #pragma unroll
   for (int it = 0; it < kSteps; ++it) {
     const int64_t e0 = base + int64_t(it) * (kThreads * 8) + threadIdx.x * 8;
     if (e0 + 8 <= vocab) {
-      const u32x4 w = load16(p + e0);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t x = w[k];
-        bad |= ((x & 0x7F80u) == 0x7F80u) | ((x & 0x7F800000u) == 0x7F800000u);
-        take(bf16_lo(x), int(e0) + 2 * k, bv, bi);
-        take(bf16_hi(x), int(e0) + 2 * k + 1, bv, bi);
-      }
+      scan8(load16(p + e0), e0);
     } else {
       for (int j = 0; j < 8; ++j) {
         const int64_t e = e0 + j;
@@ -70,6 +82,7 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks(const uint16_t* __rest
         }
       }
     }
+  }
   }
 
   // wave64 reduction, then across the block's 4 waves in wave order
