@@ -155,6 +155,7 @@ def test_markov_full_shape_parity():
     (256, 8, [(0, 1)]),
     (257, 256, [(0, 2), (2, 2), (4, 2), (6, 2), (8, 2)]),          # a partial group of four
     (1000, 24, [(i, 1) for i in range(32)]),                          # the most chains
+    (2000, 256, [(2 * i, 2) for i in range(32)]),                     # 32 chains folded a depth on
     (4099, 136, [(0, 9), (9, 9), (18, 9)]),                           # the drafter's depth
     (3000, 256, [(0, 16)]),                                           # the longest chain
 ])
