@@ -367,8 +367,8 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
   // row sees the fewest; block tables: every row sees all keys)
   const int n_first = uni(cload(tv.rows + T.row0).nkeys);
   const int n_last = uni(cload(tv.rows + T.row0 + T.nrows - 1).nkeys);
-  const int k0 = wk.split * S.split_keys;
-  const int k1 = min(k0 + S.split_keys, n_last);
+  const int k0 = split_start(S, wk.split);
+  const int k1 = min(split_start(S, wk.split + 1), n_last);
   const int64_t head_elems = int64_t(S.cap) * ASV_HEAD_DIM;
   const int64_t sel = int64_t(layer) * tv.n_streams + T.stream;
   const uint16_t* Kh = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.kp + sel))) + g * head_elems;

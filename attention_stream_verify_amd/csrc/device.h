@@ -120,7 +120,7 @@ __device__ __forceinline__ asv_seg uniform(asv_seg r) {
   const int64_t poff = int64_t((uint64_t(uint32_t(uni(int(uint32_t(p >> 32))))) << 32) |
                                uint64_t(uint32_t(uni(int(uint32_t(p))))));
   return asv_seg{uni(r.row0), uni(r.rows), uni(r.keys), uni(r.cap), uni(r.split_keys),
-                 uni(r.nsplit), poff};
+                 uni(r.nsplit), poff, uni(r.split_tail), uni(r.nbig), {0, 0}};
 }
 
 __device__ __forceinline__ uint64_t uniform_ptr(uint64_t p) {
@@ -157,6 +157,19 @@ __device__ __forceinline__ float add_xor32(float x) {
 
 // The table as the kernels see it: the uploaded blob plus the offsets that
 // asv_seg_table_build reported.
+// First key of split t of a stream (t = nsplit gives the end of the plan,
+// at or past its keys).
+__device__ __forceinline__ int split_start(const asv_seg& S, int t) {
+  return t < S.nbig ? t * S.split_keys : S.nbig * S.split_keys + (t - S.nbig) * S.split_tail;
+}
+
+// Splits of a stream that start below key n (hold a key of [0, n)), n >= 1.
+__device__ __forceinline__ int splits_before(const asv_seg& S, int n) {
+  const int big = S.nbig * S.split_keys;
+  if (n <= big) return (n + S.split_keys - 1) / S.split_keys;
+  return S.nbig + (n - big + S.split_tail - 1) / S.split_tail;
+}
+
 struct TableView {
   const asv_seg* segs;
   const asv_row* rows;

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_rows(TableView tv,
   const int h = pair - r * ASV_Q_HEADS;
   const asv_row row = uniform(cload(tv.rows + r));
   const asv_seg S = uniform(cload(tv.segs + row.stream));
-  const int nt = (row.nkeys + S.split_keys - 1) / S.split_keys;
+  const int nt = splits_before(S, row.nkeys);
   const int64_t rec0 = S.poff + int64_t(row.pos) * ASV_Q_HEADS + h;
   const int64_t step = int64_t(S.rows) * ASV_Q_HEADS;
   const float2* ml = reinterpret_cast<const float2*>(pml);

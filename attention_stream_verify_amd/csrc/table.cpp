@@ -17,12 +17,20 @@
 namespace {
 
 // Split plan of one stream, from its own rows and keys only (so a shared
-// round gives the same bits as each stream alone): the keys are cut into
-// n = ceil(keys / cap) equal splits, each rounded up to a multiple of 32
-// keys (S <= cap, and ceil(keys / S) == n). Few short windows make many
-// small splits; 16-row tiles take splits of up to 7,168 keys, which at
-// 131,072-key contexts puts one tile's 8 heads x 19 splits, and four such
-// streams' 496 work items, on the 512 blocks the device holds at once.
+// round gives the same bits as each stream alone): n = ceil(keys / cap)
+// consecutive splits, each starting at a multiple of 32 keys. Few short
+// windows make many small splits; 16-row tiles take splits of about 7,168
+// keys, which at 131,072-key contexts puts one tile's 8 heads x 19 splits,
+// and four such streams' 496 work items, on the 512 blocks the device holds
+// at once.
+//
+// Windows of up to 8 rows cut their keys into n equal splits. 16-row tiles
+// take two sizes, the first ceil(n / 2) splits 5/4 the size of the rest:
+// the work list runs the larger items first, so on a device holding two
+// blocks a CU each CU pairs a larger item with a smaller one, and the block
+// dispatched first, which streams faster (its waves win issue), has the
+// larger share; the two then finish together instead of the second block
+// running alone at the end.
 int32_t split_cap(int32_t rows) {
   const int32_t wt = rows < ASV_TILE_ROWS ? rows : ASV_TILE_ROWS;
   if (wt <= 2) return 512;
@@ -31,12 +39,32 @@ int32_t split_cap(int32_t rows) {
   return 7168;
 }
 
-int32_t split_keys_for(int32_t rows, int32_t keys) {
-  const int32_t cap = split_cap(rows);
-  const int32_t n = (keys + cap - 1) / cap;
-  const int32_t s = (keys + n - 1) / n;
-  return (s + 31) / 32 * 32;
+int32_t up32(int64_t x) { return int32_t((x + 31) / 32 * 32); }
+
+struct Plan {
+  int32_t a, b, nbig, n;  // n splits: nbig of a keys, then b keys
+};
+
+Plan split_plan(int32_t rows, int32_t keys) {
+  const int32_t n = (keys + split_cap(rows) - 1) / split_cap(rows);
+  const int32_t eq = up32((int64_t(keys) + n - 1) / n);
+  const Plan equal{eq, eq, n, n};
+  if ((rows < ASV_TILE_ROWS ? rows : ASV_TILE_ROWS) <= 8 || n == 1) return equal;
+  const int32_t nb = (n + 1) / 2;
+  const int64_t den = 5 * int64_t(nb) + 4 * int64_t(n - nb);
+  const int32_t a = up32((5 * int64_t(keys) + den - 1) / den);
+  const int64_t rest = int64_t(keys) - int64_t(nb) * a;
+  if (rest <= 0) return equal;
+  const int32_t b = up32((rest + (n - nb) - 1) / (n - nb));
+  if (int64_t(nb) * a + int64_t(n - nb - 1) * b >= keys) return equal;  // an empty split
+  return Plan{a, b, nb, n};
 }
+
+int32_t split_start(const Plan& p, int32_t t) {
+  return t < p.nbig ? t * p.a : p.nbig * p.a + (t - p.nbig) * p.b;
+}
+
+static_assert(sizeof(asv_seg) == 48, "asv_seg layout");
 
 int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
 
@@ -134,8 +162,11 @@ int build_table(const asv_stream_desc* streams, int32_t n_streams, const void* c
     g.rows = d.rows;
     g.keys = d.key_count;
     g.cap = d.kv_capacity;
-    g.split_keys = split_keys_for(d.rows, d.key_count);
-    g.nsplit = (d.key_count + g.split_keys - 1) / g.split_keys;
+    const Plan pl = split_plan(d.rows, d.key_count);
+    g.split_keys = pl.a;
+    g.nsplit = pl.n;
+    g.split_tail = pl.b;
+    g.nbig = pl.nbig;
     g.poff = poff;
     poff += int64_t(g.nsplit) * d.rows * ASV_Q_HEADS;
     for (int32_t p = 0; p < d.rows; p += ASV_TILE_ROWS) {
@@ -164,9 +195,10 @@ int build_table(const asv_stream_desc* streams, int32_t n_streams, const void* c
     const asv_tile& t = tiles[ti];
     const asv_seg& g = segs[t.stream];
     const int32_t n_last = full ? g.keys : g.keys - g.rows + t.pos0 + t.nrows;
-    for (int32_t sp = 0; int64_t(sp) * g.split_keys < n_last; ++sp) {
-      const int32_t k0 = sp * g.split_keys;
-      const int32_t k1 = std::min(k0 + g.split_keys, n_last);
+    const Plan pl{g.split_keys, g.split_tail, g.nbig, g.nsplit};
+    for (int32_t sp = 0; sp < g.nsplit && split_start(pl, sp) < n_last; ++sp) {
+      const int32_t k0 = split_start(pl, sp);
+      const int32_t k1 = std::min(sp + 1 < g.nsplit ? split_start(pl, sp + 1) : g.keys, n_last);
       for (int32_t h = 0; h < ASV_KV_HEADS; ++h) work.push_back({ti, h, sp, k1 - k0});
     }
   }

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define ASV_ABI_VERSION 1
+#define ASV_ABI_VERSION 2
 
 /* Model dimensions compiled into the kernels (LFM2.5-24B-A2B shapes). */
 #define ASV_HIDDEN 2048          /* conv channels, attention row width      */
@@ -84,13 +84,22 @@ typedef struct {      /* one per stream, caller order                     */
   int32_t rows;
   int32_t keys;
   int32_t cap;
-  int32_t split_keys; /* keys per split: the keys cut into ceil(keys/C)
-                         equal splits rounded up to 32, C = 512, 1024,
-                         2048 or 7168 by the stream's rows (<= 2, <= 4,
-                         <= 8, more)                                      */
-  int32_t nsplit;     /* ceil(keys / split_keys)                          */
+  int32_t split_keys; /* A: keys in each of the first nbig splits        */
+  int32_t nsplit;     /* n = ceil(keys / C), C = 512, 1024, 2048 or 7168
+                         by the stream's rows (<= 2, <= 4, <= 8, more)    */
   int64_t poff;       /* first partial record of the stream               */
+  int32_t split_tail; /* B: keys in each later split (the last one ends
+                         at keys)                                         */
+  int32_t nbig;       /* splits of A keys; split t starts at t*A for
+                         t < nbig, else nbig*A + (t - nbig)*B             */
+  int32_t reserved[2];
 } asv_seg;
+/* The split plan depends only on the stream's rows and keys. Windows of up
+ * to 8 rows: n equal splits, A = B = ceil(keys / n) rounded up to 32 and
+ * nbig = n. Longer windows (16-row tiles) with n >= 2: nbig = ceil(n / 2)
+ * splits of A = ceil(5 keys / (5 nbig + 4 (n - nbig))) rounded up to 32,
+ * then n - nbig splits of B = ceil((keys - nbig A) / (n - nbig)) rounded up
+ * to 32, about 4/5 of A (equal splits if that left a split empty). */
 
 typedef struct {      /* one per row                                       */
   int32_t stream;

@@ -13,8 +13,9 @@ sees every key. The pages print no formula; the readings here are:
 * score s_j = 0.125 * (q . k_j), 0.125 = 1/sqrt(64);
 * row r sees keys j < n_r (the table's causal count), softmax over them,
   output o = sum_j softmax(s)_j v_j;
-* split t of stream s covers keys [t*S_s, (t+1)*S_s) intersected with the
-  row's visible keys and gives (m_t, l_t, o_t): the max score, the sum of
+* split t of stream s covers its keys of the split plan (oracle.table)
+  intersected with the row's visible keys and gives (m_t, l_t, o_t): the
+  max score, the sum of
   exp(s_j - m_t), and the exp-weighted mean of v_j; an empty split gives
   (-inf, 0, 0);
 * the merge takes M = max_t m_t and returns
@@ -81,11 +82,11 @@ def partials(table, Q, K_list, V_list, rows=None):
     for r in rows:
         s = int(table.row_stream[r])
         n = int(table.row_nkeys[r])
-        S = int(table.split[s])
         for g in range(N_KV_HEADS):
             q = bf16.to_f64(Q[r, g * GROUP:(g + 1) * GROUP])
             for t in range(int(table.nsplit[s])):
-                lo, hi = t * S, min((t + 1) * S, n)
+                lo, hi = table.split_range(s, t)
+                hi = min(hi, n)
                 for hh in range(GROUP):
                     rec = table.record(r, g * GROUP + hh, t)
                     defined[rec] = True

@@ -15,12 +15,19 @@ definitions (the readings are listed in the design notes):
   pos = r - off_s, and sees n_r = K_s - w_s + pos + 1 keys (causal inside the
   window);
 * tiles: runs of at most 16 consecutive rows, never across streams;
-* split plan: the split size depends only on the stream's own rows and
-  keys (so a shared round gives the same bits as each stream alone): with
+* split plan: the splits depend only on the stream's own rows and keys (so
+  a shared round gives the same bits as each stream alone): with
   wt = min(w_s, 16), the cap C_s = 512 (wt <= 2), 1024 (wt <= 4),
-  2048 (wt <= 8), 7168 (otherwise); the keys are cut into
-  n_s = ceil(K_s / C_s) equal splits, S_s = ceil(K_s / n_s) rounded up to a
-  multiple of 32 (so S_s <= C_s and nsplit_s = ceil(K_s / S_s) = n_s);
+  2048 (wt <= 8), 7168 (otherwise), the keys are cut into
+  n_s = ceil(K_s / C_s) consecutive splits, each starting at a multiple of
+  32 keys, the last one ending at K_s:
+  - equal splits (wt <= 8, or n_s = 1): size S_s = ceil(K_s / n_s) rounded
+    up to a multiple of 32 (so S_s <= C_s and ceil(K_s / S_s) = n_s);
+  - otherwise two sizes: the first b_s = ceil(n_s / 2) splits of A_s keys,
+    A_s = ceil(5 K_s / (5 b_s + 4 (n_s - b_s))) rounded up to 32, and the
+    rest of B_s = ceil((K_s - b_s A_s) / (n_s - b_s)) keys rounded up to 32
+    (about 4/5 of A_s; falling back to equal splits if that left a split
+    empty, which no admitted key count does);
 * partial records: stream s owns records [poff_s, poff_s + nsplit_s*w_s*32),
   poff being the exclusive prefix sum of nsplit_s*w_s*32; the record of
   (row r, q head h, split t) is poff_s + (t*w_s + pos_r)*32 + h;
@@ -59,13 +66,32 @@ def split_cap(rows):
     return 7168
 
 
-def split_keys(rows, keys):
-    """Split size S_s: K_s keys cut into ceil(K_s / C_s) equal splits, each
-    rounded up to a multiple of 32 keys."""
-    cap = split_cap(rows)
-    n = -(-int(keys) // cap)
-    s = -(-int(keys) // n)
-    return -(-s // 32) * 32
+def _up32(x):
+    return -(-int(x) // 32) * 32
+
+
+def split_plan(rows, keys):
+    """(A, B, b, n): n splits, the first b of A keys and the rest of B keys
+    (equal splits: A = B and b = n)."""
+    K = int(keys)
+    n = -(-K // split_cap(rows))
+    equal = _up32(-(-K // n))
+    if min(int(rows), TILE_ROWS) <= 8 or n == 1:
+        return equal, equal, n, n
+    b = -(-n // 2)
+    A = _up32(-(-5 * K // (5 * b + 4 * (n - b))))
+    rest = K - b * A
+    B = _up32(-(-rest // (n - b))) if rest > 0 else 0
+    if rest <= 0 or b * A + (n - b - 1) * B >= K:
+        return equal, equal, n, n
+    return A, B, b, n
+
+
+def split_bounds(rows, keys):
+    """Start key of every split, then K_s: split t covers [bounds[t], bounds[t+1])."""
+    A, B, b, n = split_plan(rows, keys)
+    starts = [t * A for t in range(b)] + [b * A + t * B for t in range(n - b)]
+    return np.array(starts + [int(keys)], dtype=np.int64)
 
 
 @dataclass
@@ -78,8 +104,11 @@ class Table:
     row_pos: np.ndarray         # R
     row_nkeys: np.ndarray       # R
     tiles: np.ndarray           # [n_tiles, 4]: stream, first row, row count, first pos
-    split: np.ndarray           # S_s
-    nsplit: np.ndarray          # nsplit_s
+    split: np.ndarray           # A_s (S_s for equal splits)
+    nsplit: np.ndarray          # n_s
+    split_tail: np.ndarray      # B_s
+    nbig: np.ndarray            # b_s
+    bounds: list                # per stream: split starts, then K_s
     poff: np.ndarray            # S (int64)
     partial_count: int
     work: np.ndarray            # [n_work, 3]: tile, kv head, split
@@ -89,10 +118,17 @@ class Table:
         s = int(self.row_stream[r])
         return int(self.poff[s]) + (t * int(self.rows[s]) + int(self.row_pos[r])) * N_Q_HEADS + h
 
+    def splits_before(self, s, n):
+        """Splits of stream s that start below key n (hold a key of [0, n))."""
+        return int(np.count_nonzero(self.bounds[s][:-1] < int(n)))
+
     def row_nsplit(self, r):
         """Splits holding at least one key row r sees."""
-        s = int(self.row_stream[r])
-        return -(-int(self.row_nkeys[r]) // int(self.split[s]))
+        return self.splits_before(int(self.row_stream[r]), self.row_nkeys[r])
+
+    def split_range(self, s, t):
+        """Keys [lo, hi) of split t of stream s."""
+        return int(self.bounds[s][t]), int(self.bounds[s][t + 1])
 
 
 def validate(streams):
@@ -147,8 +183,12 @@ def build(streams, full=False):
             p += n
     tiles = np.array(tiles, dtype=np.int64).reshape(-1, 4)
 
-    split = np.array([split_keys(rows[s], keys[s]) for s in range(S)], dtype=np.int64)
-    nsplit = np.array([-(-keys[s] // split[s]) for s in range(S)], dtype=np.int64)
+    plans = [split_plan(rows[s], keys[s]) for s in range(S)]
+    split = np.array([p[0] for p in plans], dtype=np.int64)
+    split_tail = np.array([p[1] for p in plans], dtype=np.int64)
+    nbig = np.array([p[2] for p in plans], dtype=np.int64)
+    nsplit = np.array([p[3] for p in plans], dtype=np.int64)
+    bounds = [split_bounds(rows[s], keys[s]) for s in range(S)]
     poff = np.zeros(S, dtype=np.int64)
     acc = 0
     for s in range(S):
@@ -159,11 +199,12 @@ def build(streams, full=False):
     work = []
     for ti, (s, _r0, n, p0) in enumerate(tiles):
         n_last = keys[s] if full else keys[s] - rows[s] + p0 + n
-        for t in range(-(-int(n_last) // int(split[s]))):
+        for t in range(int(np.count_nonzero(bounds[s][:-1] < n_last))):
             for g in range(N_KV_HEADS):
                 work.append((ti, g, t))
     work = np.array(work, dtype=np.int64).reshape(-1, 3)
 
     return Table(rows=rows, keys=keys, caps=caps, seg_off=seg_off, row_stream=row_stream,
                  row_pos=row_pos, row_nkeys=row_nkeys, tiles=tiles, split=split,
-                 nsplit=nsplit, poff=poff, partial_count=partial_count, work=work, n_rows=R)
+                 nsplit=nsplit, split_tail=split_tail, nbig=nbig, bounds=bounds, poff=poff,
+                 partial_count=partial_count, work=work, n_rows=R)

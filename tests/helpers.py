@@ -128,7 +128,7 @@ def check_attention_layer(rnd, rb, partials, o_bits, li, rows, what, full=False)
         s = int(t.row_stream[r])
         tile = [tt for tt in t.tiles if tt[1] <= r < tt[1] + tt[2]][0]
         last = t.keys[s] if full else t.keys[s] - t.rows[s] + tile[3] + tile[2]
-        for sp in range(t.row_nsplit(r), -(-int(last) // int(t.split[s]))):
+        for sp in range(t.row_nsplit(r), t.splits_before(s, last)):
             for h in range(32):
                 rec = t.record(r, h, sp)
                 assert pml[rec, 0] == -np.inf and pml[rec, 1] == 0 and not po[rec].any(), what

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(asv._lib.LIB_PATH)
     for name in _declared():
         assert hasattr(L, name), name
-    assert asv.abi_version() == 1
+    assert asv.abi_version() == 2
     assert asv.strerror(-4) == "caller buffer too small"
 
 
@@ -69,6 +69,9 @@ def _compare(streams, full=False):
     assert np.array_equal(segs["cap"], o.caps)
     assert np.array_equal(segs["split_keys"], o.split)
     assert np.array_equal(segs["nsplit"], o.nsplit)
+    assert np.array_equal(segs["split_tail"], o.split_tail)
+    assert np.array_equal(segs["nbig"], o.nbig)
+    assert not segs["reserved"].any()
     assert np.array_equal(segs["poff"], o.poff)
     rows = t["rows"]
     assert np.array_equal(rows["stream"], o.row_stream)
@@ -87,7 +90,8 @@ def _compare(streams, full=False):
     for ti, h, sp, k in zip(w["tile"], w["head"], w["split"], w["keys"]):
         s, _r0, n, p0 = o.tiles[ti]
         last = o.keys[s] if full else o.keys[s] - o.rows[s] + p0 + n
-        assert k == min((sp + 1) * o.split[s], last) - sp * o.split[s] > 0
+        lo, hi = o.split_range(s, sp)
+        assert k == min(hi, last) - lo > 0
     assert np.array_equal(t["conv_state"], np.array(cs, dtype=np.uint64).ravel())
     assert np.array_equal(t["k"], np.array(kp, dtype=np.uint64).ravel())
     assert np.array_equal(t["v"], np.array(vp, dtype=np.uint64).ravel())

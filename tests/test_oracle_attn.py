@@ -144,12 +144,12 @@ def test_partials_per_split_and_merge(streams):
     assert np.allclose(merged, dense, rtol=0, atol=1e-12)
     for r in range(t.n_rows):
         s = int(t.row_stream[r])
-        S = int(t.split[s])
         n = int(t.row_nkeys[r])
         for sp in range(int(t.nsplit[s])):
             recs = [t.record(r, h, sp) for h in range(32)]
             assert defined[recs].all()
-            lo, hi = sp * S, min((sp + 1) * S, n)
+            lo, hi = t.split_range(s, sp)
+            hi = min(hi, n)
             if hi <= lo:
                 assert np.all(pm[recs] == -np.inf) and np.all(pl[recs] == 0) and np.all(po[recs] == 0)
                 continue

@@ -108,24 +108,45 @@ def test_table_split_plan_by_window():
     # the cap depends only on the stream's own rows
     assert [table.split_cap(w) for w in (1, 2, 3, 4, 5, 8, 9, 16, 17, 512)] == \
         [512, 512, 1024, 1024, 2048, 2048, 7168, 7168, 7168, 7168]
-    # equal splits, by hand: 65,536 / ceil(65,536 / 7,168) = 6,553.6 -> 6,560;
-    # 98,304 / 14 = 7,021.7 -> 7,040; 131,072 / 19 = 6,898.5 -> 6,912;
-    # 1,000 / 2 = 500 -> 512; 100 / 1 -> 128; 4,096 / 8 = 512
-    assert [table.split_keys(w, k) for (w, k) in
-            ((16, 65536), (16, 98304), (16, 131072), (1, 1000), (3, 100), (1, 4096))] == \
-        [6560, 7040, 6912, 512, 128, 512]
+    # windows of up to 8 rows, equal splits by hand: 1,000 / 2 = 500 -> 512;
+    # 100 / 1 -> 128; 4,096 / 8 = 512; 32,768 / 16 = 2,048 (cap 2,048)
+    assert [table.split_plan(w, k) for (w, k) in ((1, 1000), (3, 100), (1, 4096), (8, 32768))] == \
+        [(512, 512, 2, 2), (128, 128, 1, 1), (512, 512, 8, 8), (2048, 2048, 16, 16)]
+    # 16-row tiles, two sizes by hand (A = ceil(5K / (5b + 4(n - b))) up to 32,
+    # B = ceil((K - bA) / (n - b)) up to 32):
+    #   65,536: n = 10, b = 5: A = ceil(327,680 / 45) = 7,282 -> 7,296,
+    #           B = ceil(29,056 / 5) = 5,812 -> 5,824; last split [59,776, 65,536)
+    #   98,304: n = 14, b = 7: A = ceil(491,520 / 63) = 7,802 -> 7,808,
+    #           B = ceil(43,648 / 7) = 6,236 -> 6,240; last split [92,096, 98,304)
+    #  131,072: n = 19, b = 10: A = ceil(655,360 / 86) = 7,621 -> 7,648,
+    #           B = ceil(54,592 / 9) = 6,066 -> 6,080; last split [125,120, 131,072)
+    #    7,169: n = 2, b = 1: A = ceil(35,845 / 9) = 3,983 -> 4,000, B = 3,169 -> 3,200
+    #    7,000: n = 1: one split of 7,008
+    assert [table.split_plan(16, k) for k in (65536, 98304, 131072, 7169, 7000)] == \
+        [(7296, 5824, 5, 10), (7808, 6240, 7, 14), (7648, 6080, 10, 19), (4000, 3200, 1, 2),
+         (7008, 7008, 1, 1)]
+    assert table.split_bounds(16, 65536).tolist() == \
+        [0, 7296, 14592, 21888, 29184, 36480, 42304, 48128, 53952, 59776, 65536]
+    assert table.split_bounds(17, 131072)[-2:].tolist() == [125120, 131072]
 
 
 @settings(max_examples=300, deadline=None)
 @given(st.integers(1, 16), st.integers(1, 131072))
 def test_table_split_plan_properties(rows, keys):
     cap = table.split_cap(rows)
-    S = table.split_keys(rows, keys)
-    n = -(-keys // S)
-    assert S % 32 == 0 and S <= cap
+    A, B, b, n = table.split_plan(rows, keys)
+    bounds = table.split_bounds(rows, keys)
+    sizes = np.diff(bounds)
     assert n == -(-keys // cap)                  # as many splits as the cap forces
-    assert (n - 1) * S < keys <= n * S
-    assert n * S - keys < 32 * n + S - (keys // n)  # nearly equal: every split but the last is full
+    assert len(sizes) == n and bounds[0] == 0 and bounds[-1] == keys
+    assert (sizes > 0).all() and (bounds[:-1] % 32 == 0).all()
+    if min(rows, 16) <= 8 or n == 1:             # equal splits, every one but the last full
+        assert A == B and b == n and A % 32 == 0 and A <= cap
+        assert (sizes[:-1] == A).all() and 0 < sizes[-1] <= A
+    else:                                        # the first half 5/4 the size of the rest
+        assert b == -(-n // 2) and A % 32 == 0 and B % 32 == 0
+        assert (sizes[:b] == A).all() and (sizes[b:-1] == B).all() and 0 < sizes[-1] <= B
+        assert 1.1 < A / B < 1.45 and A <= cap * 5 // 4 + 32
 
 
 @pytest.mark.parametrize("rows,expect", [
