@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak
 WORKLOAD_NAMES = {
     0: "tiny: 4 streams, windows 1-4, keys 16-256",
     1: "decode: 16 streams x 1 row, keys 512-4096",
@@ -247,6 +248,10 @@ def main():
     order = layer_order(rnd.n_conv, rnd.n_attn)
     sum_keys = sum(k for _, k, _ in rnd.streams)
     attn_bytes = 2048 * sum_keys + 4096 * R            # K/V once + Q, per launch
+    # algorithmic attention flops a launch: q.k and p.v, 2 * 64 multiply-adds
+    # each, for every (row, q head, visible key)
+    visible = sum((k if args.block else k - w + i + 1) for w, k, _ in rnd.streams for i in range(w))
+    attn_flops = 4 * 64 * 32 * visible
     merge_bytes = 4096 * R                              # O written (partials are a means)
 
     def event():
@@ -405,6 +410,8 @@ def main():
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": None if args.block else profiled_traffic(args.config),
             "bytes_per_launch": attn_bytes,
+            "flops_per_launch": attn_flops,
+            "mfma_frac": attn_flops / (attn_avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "avg_launch_us": attn_avg_ms * 1e3,
         },
         "launch": "eager" if args.eager else "hip graph of one round",
