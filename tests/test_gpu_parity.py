@@ -200,6 +200,9 @@ def test_attention_parity(config, extra):
     [(3, 40, 64), (16, 4097, 4128), (9, 2049, 2080), (2, 513, 544)],   # ragged splits
     [(33, 600, 640), (1, 5000, 5024)],           # a 3-tile chunk
     [(512, 3000, 3072)],                         # a prompt chunk of 32 tiles
+    [(16, 7169, 7200)],                          # two split sizes: 4,000 then 3,169 keys
+    [(17, 20000, 20000)],                        # 7,168 x 2 then 5,664; a one-row second tile
+    [(16, 14337, 14368), (24, 21505, 21536)],    # 3 and 4 splits, the last one short
 ])
 def test_attention_edge_shapes(streams):
     rnd = workloads.Round(0, "cuda", n_conv=0, n_attn=1, streams=streams, with_logits=False)
@@ -318,6 +321,9 @@ def test_block_attention_parity(config, extra):
     [(3, 40, 64), (16, 4097, 4128), (9, 2049, 2080), (2, 513, 544)],   # ragged splits
     [(33, 600, 640), (1, 5000, 5024)],           # a 3-tile chunk
     [(512, 3000, 3072)],                         # a prompt chunk of 32 tiles
+    [(16, 7169, 7200)],                          # two split sizes: 4,000 then 3,169 keys
+    [(17, 20000, 20000)],                        # 7,168 x 2 then 5,664; a one-row second tile
+    [(16, 14337, 14368), (24, 21505, 21536)],    # 3 and 4 splits, the last one short
 ])
 def test_block_attention_edge_shapes(streams):
     rnd = workloads.Round(0, "cuda", n_conv=0, n_attn=1, streams=streams, with_logits=False)
