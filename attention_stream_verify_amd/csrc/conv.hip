@@ -10,8 +10,9 @@
 // Mapping: a 64-thread block covers 2 rows of one 16-row tile and 512 of the
 // 2,048 channels; each thread owns 8 channels (16-byte loads of B, C, x: one
 // block reads 1 KB contiguous per input third). Small rounds are latency
-// bound, so the grid is made wide (tiles x 8 row pairs x 4 channel groups)
-// rather than deep. Rows are independent once bx of the two rows before them
+// bound, so the grid is made wide (tiles x row pairs x 4 channel groups,
+// the row pairs of the round's largest tile) rather than deep. Rows are
+// independent once bx of the two rows before them
 // is known, so a block recomputes those from X instead of waiting for
 // another block. Only the blocks holding a stream's first two rows (the only
 // rows that read the state) touch the stream's state: each reads its
@@ -139,7 +140,11 @@ extern "C" int asv_shared_conv(const asv_table_info* info, const void* dev_blob,
     return ASV_E_ARG;
   if (layer < 0 || layer >= info->n_conv_layers) return ASV_E_SHAPE;
   const asv::TableView tv = asv::make_view(*info, dev_blob);
-  hipLaunchKernelGGL(asv::conv_rows, dim3(unsigned(info->n_tiles), asv::kSub, asv::kChannelGroups),
+  // row pairs a tile: as many as the round's largest tile needs (one for
+  // one-row decode windows), so no block is launched only to exit
+  const unsigned pairs = unsigned((info->max_tile_rows + asv::kRowsPerBlock - 1) / asv::kRowsPerBlock);
+  if (pairs < 1 || pairs > unsigned(asv::kSub)) return ASV_E_ARG;
+  hipLaunchKernelGGL(asv::conv_rows, dim3(unsigned(info->n_tiles), pairs, asv::kChannelGroups),
                      dim3(asv::kThreads),
                      0, static_cast<hipStream_t>(stream), tv, int(layer), x, w, y);
   return hipGetLastError() == hipSuccess ? ASV_OK : ASV_E_HIP;
