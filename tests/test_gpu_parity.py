@@ -203,6 +203,7 @@ def test_attention_parity(config, extra):
     [(16, 7169, 7200)],                          # two split sizes: 4,000 then 3,169 keys
     [(17, 20000, 20000)],                        # 7,168 x 2 then 5,664; a one-row second tile
     [(16, 14337, 14368), (24, 21505, 21536)],    # 3 and 4 splits, the last one short
+    [(2048, 131072, 131072)],                    # both maxima: 2,048 rows, 131,072 keys
 ])
 def test_attention_edge_shapes(streams):
     rnd = workloads.Round(0, "cuda", n_conv=0, n_attn=1, streams=streams, with_logits=False)
