@@ -18,8 +18,12 @@ def _u16(t):
     return t.detach().cpu().numpy().view(np.uint16)
 
 
-def test_graph_replays_equal_the_eager_round():
-    rnd = workloads.Round(0, device="cuda")
+@pytest.mark.parametrize("streams", [
+    None,                                               # the tiny round
+    [(16, 20000, 20000), (8, 9000, 9024), (1, 3000, 3008)],   # 16-row tiles with two split sizes
+])
+def test_graph_replays_equal_the_eager_round(streams):
+    rnd = workloads.Round(0, device="cuda", streams=streams, n_conv=1, n_attn=1)
     X, W, states = rnd.conv[0]
     Q, ks, vs = rnd.attn[0]
     rb = asv.RoundBuffers(rnd.streams, [states], [ks], [vs], device="cuda", vocab=rnd.logits.shape[1])
