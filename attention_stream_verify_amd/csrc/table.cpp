@@ -19,7 +19,9 @@ namespace {
 // Split plan of one stream, from its own rows and keys only (so a shared
 // round gives the same bits as each stream alone): n = ceil(keys / cap)
 // consecutive splits, each starting at a multiple of 32 keys. Few short
-// windows make many small splits; 16-row tiles take splits of about 7,168
+// windows make many small splits (windows of 5 to 8 rows: at most 1,536
+// keys, which evens out the 16 x 8-row verify round's items better than
+// 1,024, 1,280, 1,792 or 2,048 did); 16-row tiles take splits of about 7,168
 // keys, which at 131,072-key contexts puts one tile's 8 heads x 19 splits,
 // and four such streams' 496 work items, on the 512 blocks the device holds
 // at once.
@@ -35,7 +37,7 @@ int32_t split_cap(int32_t rows) {
   const int32_t wt = rows < ASV_TILE_ROWS ? rows : ASV_TILE_ROWS;
   if (wt <= 2) return 512;
   if (wt <= 4) return 1024;
-  if (wt <= 8) return 2048;
+  if (wt <= 8) return 1536;
   return 7168;
 }
 

@@ -18,7 +18,7 @@ definitions (the readings are listed in the design notes):
 * split plan: the splits depend only on the stream's own rows and keys (so
   a shared round gives the same bits as each stream alone): with
   wt = min(w_s, 16), the cap C_s = 512 (wt <= 2), 1024 (wt <= 4),
-  2048 (wt <= 8), 7168 (otherwise), the keys are cut into
+  1536 (wt <= 8), 7168 (otherwise), the keys are cut into
   n_s = ceil(K_s / C_s) consecutive splits, each starting at a multiple of
   32 keys, the last one ending at K_s:
   - equal splits (wt <= 8, or n_s = 1): size S_s = ceil(K_s / n_s) rounded
@@ -62,7 +62,7 @@ def split_cap(rows):
     if wt <= 4:
         return 1024
     if wt <= 8:
-        return 2048
+        return 1536
     return 7168
 
 

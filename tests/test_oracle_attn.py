@@ -133,7 +133,7 @@ def test_causality_keys_past_count_are_not_read():
 @pytest.mark.parametrize("streams", [
     [(1, 2000, 2048)],                 # 4 splits of 512
     [(3, 2500, 2560), (1, 513, 544)],  # splits of 1024 and 512, ragged ends
-    [(7, 4100, 4128)],                 # 3 splits of 2048, last one tiny
+    [(7, 4100, 4128)],                 # 3 splits of 1,376, the last 1,348 keys
     [(20, 9000, 9024)],                # two tiles, two split sizes: 5,024 then 3,976 keys
     [(16, 15000, 15008)],              # 5,376 x 2 then 4,248 keys
 ])
