@@ -19,7 +19,9 @@ namespace {
 // Split plan of one stream, from its own rows and keys only (so a shared
 // round gives the same bits as each stream alone): n = ceil(keys / cap)
 // consecutive splits, each starting at a multiple of 32 keys. Few short
-// windows make many small splits (windows of 5 to 8 rows: at most 1,536
+// windows make many small splits (one- and two-row windows: at most 768
+// keys, which puts a 16-stream decode round with 512-4,096 keys in one
+// round of the device's 512 resident blocks; windows of 5 to 8 rows: at most 1,536
 // keys, which evens out the 16 x 8-row verify round's items better than
 // 1,024, 1,280, 1,792 or 2,048 did); 16-row tiles take splits of about 7,168
 // keys, which at 131,072-key contexts puts one tile's 8 heads x 19 splits,
@@ -35,7 +37,7 @@ namespace {
 // running alone at the end.
 int32_t split_cap(int32_t rows) {
   const int32_t wt = rows < ASV_TILE_ROWS ? rows : ASV_TILE_ROWS;
-  if (wt <= 2) return 512;
+  if (wt <= 2) return 768;
   if (wt <= 4) return 1024;
   if (wt <= 8) return 1536;
   return 7168;

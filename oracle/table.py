@@ -17,7 +17,7 @@ definitions (the readings are listed in the design notes):
 * tiles: runs of at most 16 consecutive rows, never across streams;
 * split plan: the splits depend only on the stream's own rows and keys (so
   a shared round gives the same bits as each stream alone): with
-  wt = min(w_s, 16), the cap C_s = 512 (wt <= 2), 1024 (wt <= 4),
+  wt = min(w_s, 16), the cap C_s = 768 (wt <= 2), 1024 (wt <= 4),
   1536 (wt <= 8), 7168 (otherwise), the keys are cut into
   n_s = ceil(K_s / C_s) consecutive splits, each starting at a multiple of
   32 keys, the last one ending at K_s:
@@ -58,7 +58,7 @@ def split_cap(rows):
     """Largest split C_s for a stream of ``rows`` window rows."""
     wt = min(int(rows), TILE_ROWS)
     if wt <= 2:
-        return 512
+        return 768
     if wt <= 4:
         return 1024
     if wt <= 8:

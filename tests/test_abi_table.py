@@ -164,7 +164,7 @@ def test_refuses_aliasing_and_misaligned_addresses():
 
 
 def test_tables_without_layers_and_counts_at_1_32_2048_rows():
-    for streams, expect in [([(1, 4096, 4096)], 256), ([(1, 1000, 1024)] * 32, 2048),
+    for streams, expect in [([(1, 4096, 4096)], 192), ([(1, 1000, 1024)] * 32, 2048),
                             ([(16, 131072, 131072)] * 128, 128 * 16 * 32 * 19)]:
         info, _ = asv.seg_table_build(streams)
         assert info.n_rows in (1, 32, 2048) and info.partial_count == expect

@@ -131,8 +131,8 @@ def test_causality_keys_past_count_are_not_read():
 
 
 @pytest.mark.parametrize("streams", [
-    [(1, 2000, 2048)],                 # 4 splits of 512
-    [(3, 2500, 2560), (1, 513, 544)],  # splits of 1024 and 512, ragged ends
+    [(1, 2500, 2560)],                 # 4 splits of 640
+    [(3, 2500, 2560), (1, 513, 544)],  # 3 splits of 864, one of 513, ragged ends
     [(7, 4100, 4128)],                 # 3 splits of 1,376, the last 1,348 keys
     [(20, 9000, 9024)],                # two tiles, two split sizes: 5,024 then 3,976 keys
     [(16, 15000, 15008)],              # 5,376 x 2 then 4,248 keys
@@ -178,7 +178,7 @@ def test_shared_round_rows_equal_each_stream_alone():
 
 
 def test_merge_skips_empty_splits_and_propagates_nan():
-    streams = [(1, 2000, 2048)]                      # 4 splits of 512
+    streams = [(1, 2500, 2560)]                      # 4 splits of 640
     t, Q, K, V = _round(streams, 8)
     po, pm, pl, _ = attn.partials(t, Q, K, V)
     base = attn.merge(t, po, pm, pl)
