@@ -170,7 +170,8 @@ def cpu_baseline(rnd, R, full=False):
     t3 = time.perf_counter()
     t_round = rnd.n_conv * (t1 - t0) + rnd.n_attn * (t2 - t1) + (t3 - t2)
     return {
-        "value": R / t_round, "unit": "rows/s", "cores": int(cores), "kind": "oracle",
+        "value": R / t_round, "unit": "rows/s", "cores": int(cores), "host_cpus": os.cpu_count(),
+        "kind": "oracle",
         "sample": (f"one conv layer ({t1 - t0:.2f} s), one attention layer with partials "
                    f"and merge ({t2 - t1:.2f} s) and the argmax ({t3 - t2:.2f} s) over all "
                    f"{R} rows of this workload, scaled by {rnd.n_conv}/{rnd.n_attn}/1 "
