@@ -24,27 +24,14 @@
 // Scan: one thread per token v, 256 tokens a block. W2 is stored
 // chunk-major ([rank/8][vocab][8]: the 8 coefficients k = 8c..8c+7 of token
 // v at chunk c), so one 16-byte load per lane per chunk is a contiguous 1 KB
-// per wave; a lane issues all rank/8 loads of its token first (up to 128
-// VGPRs, 32 KB a wave in flight). The chains' W1 rows are the same for the
-// whole block: they are converted to float32 into LDS once, and each
+// per wave; a lane holds all rank/8 chunks of its token (up to 128 VGPRs,
+// 32 KB a wave in flight), requested in two halves with the chains' W1
+// pieces between them, so the W1 rows are ready while the second half
+// still streams. The chains' W1 rows are the same for the whole block:
+// they are converted to float32 into LDS once, and each
 // multiply-add reads its W1 value by an LDS broadcast. The dot is summed one
 // k at a time in float32 (a fused multiply-add of an exact product), four
 // chains at a time so that each converted W2 value serves four chains.
-// One step is two launches, no atomics: every chain's row at depth j is
-// scored by one scan launch and folded by a one-block launch, which writes
-// the picks that the next step's scan reads as previous tokens.
-//
-// Scan: one thread per token v, 256 tokens a block. W2 is stored
-// chunk-major ([rank/8][vocab][8]: the 8 coefficients k = 8c..8c+7 of token
-// v at chunk c), so one 16-byte load per lane per chunk is a contiguous 1 KB
-// per wave; a lane issues all rank/8 loads of its token first (up to 128
-// VGPRs, 32 KB a wave in flight). The previous token and W1's row are the
-// same for the whole grid, so they are read through the constant address
-// space into scalar registers, and each multiply-add takes its W1 value from
-// an SGPR. The dot is summed one k at a time in float32 (a fused
-// multiply-add of an exact product), four chains at a time so that each
-// converted W2 value serves four chains. The block's best (score, token) per
-// chain and its nonfinite flag go to the workspace.
 
 #include <array>
 #include <climits>
