@@ -157,6 +157,17 @@ __global__ __launch_bounds__(kThreads, 2) void markov_scan(Step st, const uint16
   const bool live = v < vocab;
   const int vc = live ? v : vocab - 1;
 
+  // Thread i < n's source, read with wave-uniform indexes (scalar loads of
+  // the kernel argument), and at the first depth its previous token from
+  // prev0: both requested before the W2 loads, since vector loads retire in
+  // order and a later wait for them would wait for W2 too.
+  int my_src = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxChains; ++i)
+    if (i == tid) my_src = st.src[i];
+  int my_prev = 0;
+  if (tid < st.n && my_src < 0) my_prev = gload(prev0 + (-1 - my_src));
+
   // The depth before: wave w folds its chains w, w + 4, ...; the first
   // chain's records are requested before the W2 loads, so waiting for them
   // does not wait for W2.
@@ -178,36 +189,47 @@ __global__ __launch_bounds__(kThreads, 2) void markov_scan(Step st, const uint16
   for (int c = 0; c < kHalf; ++c) w[c] = load16(wp + c * plane);
   __builtin_amdgcn_sched_barrier(0);
 
-  for (int ci = wave; ci < nfold; ci += kThreads / 64) {
-    const uint32_t* r = prec + int64_t(ci) * nblocks;
-    if (ci != wave) {
-      fa = FoldAcc{0u, 0u, false};
-      fold_load(fe, r, nblocks, 0, lane);
-    }
-    fold_use(fa, fe, 0, lane);
-    for (int b0 = 64 * 8; b0 < nblocks; b0 += 64 * 8) {
-      fold_load(fe, r, nblocks, b0, lane);
-      fold_use(fa, fe, b0, lane);
-    }
+  // chain ci's fold result: its previous token for this block, and block 0
+  // writes it as the depth before's pick
+  auto fold_done = [&](int ci, FoldAcc a) {
     uint32_t tok;
     bool bad;
-    fold_finish(fa, tok, bad);
+    fold_finish(a, tok, bad);
     if (lane == 0) {
       s_ptok[ci] = int32_t(tok);
       if (blockIdx.x == 0) {
-        gstore(pick + st.prow[ci], int32_t(tok));
-        gstore(flag + st.prow[ci], uint8_t(bad ? 1 : 0));
+        // ci is wave-uniform: a scalar read of the row, not a vector load
+        // whose wait would wait for the W2 loads in flight
+        const int pr = st.prow[__builtin_amdgcn_readfirstlane(ci)];
+        gstore(pick + pr, int32_t(tok));
+        gstore(flag + pr, uint8_t(bad ? 1 : 0));
       }
     }
+  };
+  // The first chain apart from the loop below, so that its wait (on the
+  // records only) is not merged with the reloads' waits (on everything).
+  if (fold_first) {
+    fold_use(fa, fe, 0, lane);
+    for (int b0 = 64 * 8; b0 < nblocks; b0 += 64 * 8) {
+      fold_load(fe, prec + int64_t(wave) * nblocks, nblocks, b0, lane);
+      fold_use(fa, fe, b0, lane);
+    }
+    fold_done(wave, fa);
+  }
+  for (int ci = wave + kThreads / 64; ci < nfold; ci += kThreads / 64) {
+    const uint32_t* r = prec + int64_t(ci) * nblocks;
+    FoldAcc a{0u, 0u, false};
+    for (int b0 = 0; b0 < nblocks; b0 += 64 * 8) {
+      fold_load(fe, r, nblocks, b0, lane);
+      fold_use(a, fe, b0, lane);
+    }
+    fold_done(ci, a);
   }
   __syncthreads();
 
   // previous tokens, then the chains' W1 rows in float32 (row 0 stands in
   // for an invalid token: its sum is replaced by +0)
-  if (tid < st.n) {
-    const int src = st.src[tid];
-    s_prev[tid] = src >= 0 ? s_ptok[src] : cload(prev0 + (-1 - src));
-  }
+  if (tid < st.n) s_prev[tid] = my_src >= 0 ? s_ptok[my_src] : my_prev;
   __syncthreads();
   // one 16-byte piece of a W1 row a thread and pass (n * rank / 8 pieces,
   // at most 1,024: four passes), all requested before the second W2 half
@@ -243,10 +265,6 @@ __global__ __launch_bounds__(kThreads, 2) void markov_scan(Step st, const uint16
   __syncthreads();
 
   for (int g = 0; g < st.n; g += kGroup) {
-    // Keep W2 as raw bf16 pairs between groups (128 VGPRs); converting it
-    // once for every group would hold 256 floats and spill.
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) asm volatile("" : "+v"(w[c]));
     bool ok[kGroup];
     uint32_t bv[kGroup];
     int cs[kGroup];
@@ -255,12 +273,19 @@ __global__ __launch_bounds__(kThreads, 2) void markov_scan(Step st, const uint16
       cs[i] = min(g + i, st.n - 1);
       const int p = s_prev[cs[i]];
       ok[i] = p >= 0 && p < vocab;
-      bv[i] = live ? uint32_t(gload(base + int64_t(st.row[cs[i]]) * stride + v)) : 0u;
+      // unconditional (a lane past the vocabulary reads the last token and
+      // is not scored), so no branch makes the compiler wait for it early
+      bv[i] = uint32_t(gload(base + int64_t(st.row[cs[i]]) * stride + vc));
     }
 
     float acc[kGroup] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
+      // Keep W2 as raw bf16 pairs between groups (128 VGPRs): converting it
+      // once for every group would hold 256 floats and spill. The pin sits
+      // at each chunk's use, so chunk c waits for its own load only and the
+      // first chunks are scored while the later ones stream in.
+      asm volatile("" : "+v"(w[c]));
       float f[8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
