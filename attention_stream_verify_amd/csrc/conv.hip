@@ -14,7 +14,9 @@
 // the row pairs of the round's largest tile) rather than deep. Rows are
 // independent once bx of the two rows before them
 // is known, so a block recomputes those from X instead of waiting for
-// another block. Only the blocks holding a stream's first two rows (the only
+// another block. A block issues all of its loads (rows, taps, history, and
+// the rows the new state needs) as soon as its tile record is read, so it
+// waits for memory once. Only the blocks holding a stream's first two rows (the only
 // rows that read the state) touch the stream's state: each reads its
 // channels of the state, then writes them anew, so no thread ever reads a
 // state that another thread is rewriting.
@@ -29,14 +31,21 @@ constexpr int kChannelGroups = ASV_HIDDEN / (kThreads * 8);
 constexpr int kRowsPerBlock = 2;
 constexpr int kSub = ASV_TILE_ROWS / kRowsPerBlock;
 
-// bx for 8 channels of one row: bf16(B * x), exact product in fp32.
-__device__ __forceinline__ void bx8(const uint16_t* xrow, int c0, float out[8]) {
-  const u32x4 b = load16(xrow + c0);
-  const u32x4 x = load16(xrow + 2 * ASV_HIDDEN + c0);
+// bx for 8 channels of one row from its loaded B and x words: bf16(B * x),
+// the exact product in fp32 rounded once.
+__device__ __forceinline__ void bx8(const u32x4& b, const u32x4& x, float out[8]) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     out[2 * k] = bf16_to_f32(uint16_t(f32_to_bf16(bf16_lo(b[k]) * bf16_lo(x[k]))));
     out[2 * k + 1] = bf16_to_f32(uint16_t(f32_to_bf16(bf16_hi(b[k]) * bf16_hi(x[k]))));
+  }
+}
+
+__device__ __forceinline__ void words8(const u32x4& w, float out[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    out[2 * k] = bf16_lo(w[k]);
+    out[2 * k + 1] = bf16_hi(w[k]);
   }
 }
 
@@ -47,25 +56,93 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* p, const float v[8]) {
   store16(p, w);
 }
 
+// One row: y = C * (w0 h0 + w1 h1 + w2 bx) for 8 channels, then the history
+// moves on by one step.
+__device__ __forceinline__ void conv_row(const u32x4& b, const u32x4& c, const u32x4& x, const float w0[8],
+                                         const float w1[8], const float w2[8], float h0[8], float h1[8],
+                                         uint16_t* yrow) {
+  float bx[8];
+  bx8(b, x, bx);
+  float y[8];
+#pragma unroll
+  for (int ch = 0; ch < 8; ++ch) {
+    const float gate = (ch & 1) ? bf16_hi(c[ch >> 1]) : bf16_lo(c[ch >> 1]);
+    float acc = w0[ch] * h0[ch];
+    acc = __builtin_fmaf(w1[ch], h1[ch], acc);
+    acc = __builtin_fmaf(w2[ch], bx[ch], acc);
+    y[ch] = __uint_as_float(f32_to_bf16(gate * acc) << 16);
+    h0[ch] = h1[ch];
+    h1[ch] = bx[ch];
+  }
+  store_bf16x8(yrow, y);
+}
+
 __global__ __launch_bounds__(kThreads) void conv_rows(TableView tv, int layer,
                                                       const uint16_t* __restrict__ X,
                                                       const uint16_t* __restrict__ W,
                                                       uint16_t* __restrict__ Y) {
-  const asv_tile T = gload(tv.tiles + blockIdx.x);
+  static_assert(kRowsPerBlock == 2, "a block holds one or two rows");
+  // The launch arguments the block uses, read into scalar registers together
+  // with the tile pointer (otherwise each is read where first used, after
+  // the early exit below, one round trip after another).
+  const asv_seg* segs = tv.segs;
+  const uint64_t* cstate = tv.conv_state;
+  const int nstreams = tv.n_streams;
+  asm volatile("" ::"s"(segs), "s"(cstate), "s"(nstreams), "s"(layer), "s"(X), "s"(W), "s"(Y));
+  const asv_tile T = cload(tv.tiles + blockIdx.x);
   const int i0 = blockIdx.y * kRowsPerBlock;
   if (i0 >= T.nrows) return;
-  const int i1 = min(i0 + kRowsPerBlock, T.nrows);
-  const asv_seg S = gload(tv.segs + T.stream);
-  const int p0 = T.pos0 + i0;           // window position of the block's first row
+  const bool two = i0 + 1 < T.nrows;
+  const int p0 = T.pos0 + i0;           // window position of the block's first row (even)
   const int c0 = (blockIdx.z * kThreads + threadIdx.x) * 8;
+  const int64_t r0 = int64_t(T.row0) + i0;
+
+  // Every load of the block is issued before any is waited for, so the
+  // block pays one memory round trip: its rows' B, C, x (a missing second
+  // row re-reads the first), the taps, and the history: bx of the two rows
+  // before the block (rows r0 - 2, r0 - 1 of the same stream when p0 >= 2),
+  // or, for a stream's first rows, its state and, when the stream has rows
+  // past the block, its last two rows for the new state. The history
+  // addresses are selected rather than branched on; a load a block does
+  // not need re-reads an address it reads anyway.
+  const uint16_t* xa = X + r0 * ASV_CONV_IN;
+  const uint16_t* xb = xa + (two ? ASV_CONV_IN : 0);
+  const bool first = p0 == 0;
+  // the stream record and the state pointer in one round trip
+  const asv_seg S = cload(segs + T.stream);
+  uint16_t* state = reinterpret_cast<uint16_t*>(cload(cstate + int64_t(layer) * nstreams + T.stream));
+  asm volatile("" : "+s"(state) : "s"(S.row0), "s"(S.rows));
+  const bool tail = first && (two ? 2 : 1) != S.rows;
+  const u32x4 ba = load16(xa + c0), ca = load16(xa + ASV_HIDDEN + c0), xa2 = load16(xa + 2 * ASV_HIDDEN + c0);
+  const u32x4 bb = load16(xb + c0), cb = load16(xb + ASV_HIDDEN + c0), xb2 = load16(xb + 2 * ASV_HIDDEN + c0);
+  const u32x4 wa = load16(W + c0 * 3), wb = load16(W + c0 * 3 + 8), wc = load16(W + c0 * 3 + 16);
+  // p0 >= 2: B and x of rows r0 - 2, r0 - 1; p0 == 0: the state's two steps (in hb0 and hb1)
+  // (each selected address passes through an empty asm, so the compiler
+  // cannot see which operand it is: it would otherwise merge a re-read with
+  // the load it repeats, or turn the select back into a branch)
+  const uint16_t* h0 = first ? state : xa - 2 * ASV_CONV_IN;
+  const uint16_t* h1 = first ? state + ASV_HIDDEN : xa - ASV_CONV_IN;
+  int hx = first ? 0 : 2 * ASV_HIDDEN;
+  asm("" : "+s"(h0), "+s"(h1), "+s"(hx));
+  const u32x4 hb0 = load16(h0 + c0), hx0 = load16(h0 + hx + c0);
+  const u32x4 hb1 = load16(h1 + c0), hx1 = load16(h1 + hx + c0);
+  // B and x of the stream's last two rows when the new state needs them
+  const uint16_t* xl = tail ? X + (int64_t(S.row0) + S.rows - 2) * ASV_CONV_IN : xa;
+  int ln = tail ? ASV_CONV_IN : 0;
+  asm("" : "+s"(xl), "+s"(ln));
+  const u32x4 lb0 = load16(xl + c0), lx0 = load16(xl + 2 * ASV_HIDDEN + c0);
+  const u32x4 lb1 = load16(xl + ln + c0), lx1 = load16(xl + ln + 2 * ASV_HIDDEN + c0);
+  // Compiler-only barriers: no memory access (asm) and no instruction
+  // (sched_barrier) moves across them, so the loads above are all issued
+  // before any of their results is waited for (neither makes the hardware
+  // wait for anything).
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 
   // taps of 8 channels: W[c][0..2] for c = c0..c0+7, 48 contiguous bytes
   float w0[8], w1[8], w2[8];
   {
-    const u32x4 a = load16(W + c0 * 3);
-    const u32x4 b = load16(W + c0 * 3 + 8);
-    const u32x4 c = load16(W + c0 * 3 + 16);
-    uint32_t words[12] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], c[0], c[1], c[2], c[3]};
+    const uint32_t words[12] = {wa[0], wa[1], wa[2], wa[3], wb[0], wb[1], wb[2], wb[3], wc[0], wc[1], wc[2], wc[3]};
 #pragma unroll
     for (int ch = 0; ch < 8; ++ch) {
 #pragma unroll
@@ -79,53 +156,25 @@ __global__ __launch_bounds__(kThreads) void conv_rows(TableView tv, int layer,
     }
   }
 
-  uint16_t* state = reinterpret_cast<uint16_t*>(
-      gload(tv.conv_state + int64_t(layer) * tv.n_streams + T.stream));
-  float h0[8], h1[8];
-  if (p0 == 0) {
-    const u32x4 s0 = load16(state + c0);
-    const u32x4 s1 = load16(state + ASV_HIDDEN + c0);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      h0[2 * k] = bf16_lo(s0[k]);
-      h0[2 * k + 1] = bf16_hi(s0[k]);
-      h1[2 * k] = bf16_lo(s1[k]);
-      h1[2 * k + 1] = bf16_hi(s1[k]);
-    }
+  float g0[8], g1[8];   // the two history steps before the next row
+  if (first) {
+    words8(hb0, g0);
+    words8(hb1, g1);
   } else {
-    // p0 >= 2: the two history steps before the block are bx of rows p0-2, p0-1
-    bx8(X + int64_t(S.row0 + p0 - 2) * ASV_CONV_IN, c0, h0);
-    bx8(X + int64_t(S.row0 + p0 - 1) * ASV_CONV_IN, c0, h1);
+    bx8(hb0, hx0, g0);
+    bx8(hb1, hx1, g1);
   }
+  conv_row(ba, ca, xa2, w0, w1, w2, g0, g1, Y + r0 * ASV_HIDDEN + c0);
+  if (two) conv_row(bb, cb, xb2, w0, w1, w2, g0, g1, Y + (r0 + 1) * ASV_HIDDEN + c0);
 
-  for (int i = i0; i < i1; ++i) {
-    const int64_t r = T.row0 + i;
-    const uint16_t* xr = X + r * ASV_CONV_IN;
-    const u32x4 cw = load16(xr + ASV_HIDDEN + c0);
-    float bx[8];
-    bx8(xr, c0, bx);
-    float y[8];
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) {
-      const float gate = (ch & 1) ? bf16_hi(cw[ch >> 1]) : bf16_lo(cw[ch >> 1]);
-      float acc = w0[ch] * h0[ch];
-      acc = __builtin_fmaf(w1[ch], h1[ch], acc);
-      acc = __builtin_fmaf(w2[ch], bx[ch], acc);
-      y[ch] = __uint_as_float(f32_to_bf16(gate * acc) << 16);
-      h0[ch] = h1[ch];
-      h1[ch] = bx[ch];
-    }
-    store_bf16x8(Y + r * ASV_HIDDEN + c0, y);
-  }
-
-  if (p0 == 0) {
+  if (first) {
     // new state = the last two history steps [h_w, h_{w+1}]
-    if (T.pos0 + i1 != S.rows) {
-      bx8(X + int64_t(S.row0 + S.rows - 2) * ASV_CONV_IN, c0, h0);
-      bx8(X + int64_t(S.row0 + S.rows - 1) * ASV_CONV_IN, c0, h1);
+    if (tail) {
+      bx8(lb0, lx0, g0);
+      bx8(lb1, lx1, g1);
     }
-    store_bf16x8(state + c0, h0);
-    store_bf16x8(state + ASV_HIDDEN + c0, h1);
+    store_bf16x8(state + c0, g0);
+    store_bf16x8(state + ASV_HIDDEN + c0, g1);
   }
 }
 

@@ -154,6 +154,25 @@ def test_conv_parity(config):
         assert np.array_equal(host_u16(st), st_ref[s]), f"state of stream {s}"
 
 
+@pytest.mark.parametrize("streams", [
+    [(1, 40, 64), (2, 40, 64), (3, 40, 64), (4, 40, 64)],            # state only, state + tail rows
+    [(15, 100, 128), (16, 100, 128), (17, 100, 128), (33, 100, 128)],  # ragged tiles and one-row tiles
+])
+def test_conv_parity_ragged_windows(streams):
+    """Each stream's first block (state in, last rows for the new state) and
+    the blocks past it (history recomputed from the rows before), at window
+    sizes around the two-row block and the 16-row tile."""
+    rnd = workloads.Round(0, "cuda", n_conv=1, n_attn=0, streams=streams, with_logits=False)
+    X, W, states = rnd.conv[0]
+    before = [host_u16(s) for s in states]
+    _, out = run_round(rnd, with_argmax=False)
+    t = otable.build(streams)
+    y_ref, st_ref = oconv.shared_conv(t, host_u16(X), host_u16(W), before)
+    check_bf16_out(host_u16(out["y"][0]), y_ref, f"conv {streams}")
+    for s, st in enumerate(states):
+        assert np.array_equal(host_u16(st), st_ref[s]), f"state of stream {s}"
+
+
 def test_conv_window_equals_one_row_rounds():
     """A window of w rows equals w one-row rounds carried through the state."""
     import attention_stream_verify_amd as asv
