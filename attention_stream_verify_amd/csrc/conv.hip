@@ -108,11 +108,17 @@ __global__ __launch_bounds__(kThreads) void conv_rows(TableView tv, int layer,
   const uint16_t* xa = X + r0 * ASV_CONV_IN;
   const uint16_t* xb = xa + (two ? ASV_CONV_IN : 0);
   const bool first = p0 == 0;
-  // the stream record and the state pointer in one round trip
-  const asv_seg S = cload(segs + T.stream);
+  // the stream record and the state pointer in one round trip: both pass
+  // through one asm, so nothing computed from either can be moved ahead of
+  // the other's read
+  // (only the record's first 8 bytes, row0 and rows: a 16-byte read with two
+  // dead words lets the compiler reuse those registers, which then waits)
+  static_assert(offsetof(asv_seg, row0) == 0 && offsetof(asv_seg, rows) == 4, "asv_seg layout");
+  const uint64_t rr = cload(reinterpret_cast<const uint64_t*>(segs + T.stream));
   uint16_t* state = reinterpret_cast<uint16_t*>(cload(cstate + int64_t(layer) * nstreams + T.stream));
-  asm volatile("" : "+s"(state) : "s"(S.row0), "s"(S.rows));
-  const bool tail = first && (two ? 2 : 1) != S.rows;
+  int srow0 = int(uint32_t(rr)), srows = int(uint32_t(rr >> 32));
+  asm volatile("" : "+s"(state), "+s"(srow0), "+s"(srows));
+  const bool tail = first && (two ? 2 : 1) != srows;
   const u32x4 ba = load16(xa + c0), ca = load16(xa + ASV_HIDDEN + c0), xa2 = load16(xa + 2 * ASV_HIDDEN + c0);
   const u32x4 bb = load16(xb + c0), cb = load16(xb + ASV_HIDDEN + c0), xb2 = load16(xb + 2 * ASV_HIDDEN + c0);
   const u32x4 wa = load16(W + c0 * 3), wb = load16(W + c0 * 3 + 8), wc = load16(W + c0 * 3 + 16);
@@ -127,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void conv_rows(TableView tv, int layer,
   const u32x4 hb0 = load16(h0 + c0), hx0 = load16(h0 + hx + c0);
   const u32x4 hb1 = load16(h1 + c0), hx1 = load16(h1 + hx + c0);
   // B and x of the stream's last two rows when the new state needs them
-  const uint16_t* xl = tail ? X + (int64_t(S.row0) + S.rows - 2) * ASV_CONV_IN : xa;
+  const uint16_t* xl = tail ? X + (int64_t(srow0) + srows - 2) * ASV_CONV_IN : xa;
   int ln = tail ? ASV_CONV_IN : 0;
   asm("" : "+s"(xl), "+s"(ln));
   const u32x4 lb0 = load16(xl + c0), lx0 = load16(xl + 2 * ASV_HIDDEN + c0);
