@@ -108,11 +108,11 @@ __global__ __launch_bounds__(kThreads) void conv_rows(TableView tv, int layer,
   const uint16_t* xa = X + r0 * ASV_CONV_IN;
   const uint16_t* xb = xa + (two ? ASV_CONV_IN : 0);
   const bool first = p0 == 0;
-  // the stream record and the state pointer in one round trip: both pass
-  // through one asm, so nothing computed from either can be moved ahead of
-  // the other's read
-  // (only the record's first 8 bytes, row0 and rows: a 16-byte read with two
-  // dead words lets the compiler reuse those registers, which then waits)
+  // The stream's row0 and rows and its state pointer in one round trip:
+  // the values pass through one asm, so nothing computed from either moves
+  // ahead of the other's read. Only the record's first 8 bytes are read: a
+  // 16-byte read leaves two dead words whose registers the compiler reuses
+  // for the pointer's address, waiting for the record first.
   static_assert(offsetof(asv_seg, row0) == 0 && offsetof(asv_seg, rows) == 4, "asv_seg layout");
   const uint64_t rr = cload(reinterpret_cast<const uint64_t*>(segs + T.stream));
   uint16_t* state = reinterpret_cast<uint16_t*>(cload(cstate + int64_t(layer) * nstreams + T.stream));
@@ -122,10 +122,11 @@ __global__ __launch_bounds__(kThreads) void conv_rows(TableView tv, int layer,
   const u32x4 ba = load16(xa + c0), ca = load16(xa + ASV_HIDDEN + c0), xa2 = load16(xa + 2 * ASV_HIDDEN + c0);
   const u32x4 bb = load16(xb + c0), cb = load16(xb + ASV_HIDDEN + c0), xb2 = load16(xb + 2 * ASV_HIDDEN + c0);
   const u32x4 wa = load16(W + c0 * 3), wb = load16(W + c0 * 3 + 8), wc = load16(W + c0 * 3 + 16);
-  // p0 >= 2: B and x of rows r0 - 2, r0 - 1; p0 == 0: the state's two steps (in hb0 and hb1)
-  // (each selected address passes through an empty asm, so the compiler
-  // cannot see which operand it is: it would otherwise merge a re-read with
-  // the load it repeats, or turn the select back into a branch)
+  // History: p0 >= 2, B and x of rows r0 - 2 and r0 - 1; p0 == 0, the
+  // state's two steps (hb0, hb1; hx0 and hx1 re-read them). Each selected
+  // address passes through an empty asm, so the compiler cannot see which
+  // operand it is: it would otherwise merge a re-read with the load it
+  // repeats, or turn the select back into a branch.
   const uint16_t* h0 = first ? state : xa - 2 * ASV_CONV_IN;
   const uint16_t* h1 = first ? state + ASV_HIDDEN : xa - ASV_CONV_IN;
   int hx = first ? 0 : 2 * ASV_HIDDEN;
