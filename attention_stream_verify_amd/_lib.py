@@ -297,7 +297,7 @@ def markov_workspace(vocab):
 
 
 def markov_pack_w2(w2, vocab, rank, w2c, stream=None):
-    """W2 [vocab][rank] bf16 -> the chunk-major layout markov_pick reads."""
+    """W2 [vocab][rank] bf16 -> the tiled layout markov_pick reads (64-token tiles, each [rank/8][tile][8])."""
     _check(lib().asv_markov_pack_w2(_addr(w2), int(vocab), int(rank), _addr(w2c), _stream(stream)),
            "asv_markov_pack_w2")
 

@@ -21,10 +21,12 @@
 // between the two halves of the workspace, so no block overwrites records
 // that another block of the same launch still folds.
 //
-// Scan: one thread per token v, 256 tokens a block. W2 is stored
-// chunk-major ([rank/8][vocab][8]: the 8 coefficients k = 8c..8c+7 of token
-// v at chunk c), so one 16-byte load per lane per chunk is a contiguous 1 KB
-// per wave; a lane holds all rank/8 chunks of its token (up to 128 VGPRs,
+// Scan: one thread per token v, 256 tokens a block. W2 is stored in tiles
+// of 64 tokens (one wave's), each [rank/8][64][8]: the 8 coefficients
+// k = 8c..8c+7 of the tile's tokens at chunk c, so one 16-byte load per lane
+// per chunk is a contiguous 1 KB, and a wave's rank/8 loads are one
+// contiguous run of rank * 128 bytes (faster than chunks a whole vocabulary
+// apart). A lane holds all rank/8 chunks of its token (up to 128 VGPRs,
 // 32 KB a wave in flight), requested in two halves with the chains' W1
 // pieces between them, so the W1 rows are ready while the second half
 // still streams. The chains' W1 rows are the same for the whole block:
@@ -183,8 +185,12 @@ __global__ __launch_bounds__(kThreads, 2) void markov_scan(Step st, const uint16
   // is scored while the second streams in (load counts retire in order)
   constexpr int kHalf = (NCH + 1) / 2;
   u32x4 w[NCH];
-  const uint16_t* wp = w2c + int64_t(vc) * 8;
-  const int64_t plane = int64_t(vocab) * 8;
+  // the wave's 64-token tile of W2: chunk c of its tokens at c * tl * 8 from
+  // the tile's start, tl = the tile's token count (64 but in the last tile)
+  const int64_t tile = vc / 64;
+  const int64_t tl = min(int64_t(64), int64_t(vocab) - tile * 64);
+  const uint16_t* wp = w2c + tile * 64 * rank + (vc - tile * 64) * 8;
+  const int64_t plane = tl * 8;
 #pragma unroll
   for (int c = 0; c < kHalf; ++c) w[c] = load16(wp + c * plane);
   __builtin_amdgcn_sched_barrier(0);
@@ -363,14 +369,17 @@ __global__ __launch_bounds__(kThreads) void markov_fold(Step st, int nblocks,
   }
 }
 
-// W2 [vocab][rank] -> chunk-major [rank/8][vocab][8], one 16-byte chunk a thread.
+// W2 [vocab][rank] -> tiles of 64 tokens, each [rank/8][tl][8] (tl = the
+// tile's token count), one 16-byte chunk a thread.
 __global__ __launch_bounds__(kThreads) void markov_pack(const uint16_t* __restrict__ w2, int64_t vocab,
                                                         int nch, uint16_t* __restrict__ w2c) {
   const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (t >= vocab * nch) return;
   const int64_t v = t / nch;
   const int64_t c = t - v * nch;
-  store16(w2c + (c * vocab + v) * 8, load16(w2 + t * 8));
+  const int64_t tile = v / 64;
+  const int64_t tl = min(int64_t(64), vocab - tile * 64);
+  store16(w2c + (tile * 64 * nch + c * tl + (v - tile * 64)) * 8, load16(w2 + t * 8));
 }
 
 int64_t scan_blocks(int64_t vocab) { return (vocab + kThreads - 1) / kThreads; }

@@ -85,8 +85,10 @@ int asv_draft_ids(const asv_draft_span* spans, int32_t n_streams, const int32_t*
  *   chains     HOST, asv_markov_chain [n_chains]; rows in range, disjoint
  *   prev0      device, int32 [n_chains] (each chain's first previous token)
  *   w1         device, bf16 [vocab][rank], 16-byte aligned
- *   w2c        device, bf16 W2 chunk-major [rank/8][vocab][8]: element
- *              (v, k) at ((k / 8) * vocab + v) * 8 + k % 8 (asv_markov_pack_w2)
+ *   w2c        device, bf16 W2 in tiles of 64 tokens, each [rank/8][tl][8]
+ *              (tl = 64, or vocab % 64 for a shorter last tile): element
+ *              (v, k) at (64 * rank * t + (k / 8) * tl + v - 64 t) * 8 + k % 8,
+ *              t = v / 64 (asv_markov_pack_w2); vocab * rank elements
  *   pick, flag device, int32 / uint8 [rows]
  *   workspace  device, asv_markov_workspace(vocab) bytes, 16-byte aligned;
  *              one call at a time per workspace (two halves of one 4-byte
@@ -109,7 +111,7 @@ int asv_markov_pick(const uint16_t* base, int64_t rows, int64_t row_stride,
                     void* stream);
 
 /* W2 [vocab][rank] (row-major bf16, as the checkpoint holds it) into the
- * chunk-major layout asv_markov_pick reads; once, when the weights load.
+ * tiled layout asv_markov_pick reads; once, when the weights load.
  * Plain data movement, no arithmetic. Errors: ASV_E_SHAPE (vocab),
  * ASV_E_UNSUPPORTED (rank), ASV_E_ARG (null, misaligned or overlapping). */
 int asv_markov_pack_w2(const uint16_t* w2, int64_t vocab, int32_t rank, uint16_t* w2c,

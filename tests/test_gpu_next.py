@@ -127,15 +127,18 @@ def _check_markov(base, chains, prev0, w1, w2):
     return gp, gf
 
 
-def test_markov_pack_is_the_chunk_major_layout():
+def test_markov_pack_is_the_tiled_layout():
+    """Tiles of 64 tokens, each [rank/8][tokens of the tile][8], the last
+    tile shorter when 64 does not divide the vocabulary."""
     rng = np.random.default_rng(11)
-    for vocab, rank in [(1, 8), (1000, 24), (4099, 256)]:
+    for vocab, rank in [(1, 8), (64, 8), (1000, 24), (4099, 256)]:
         w2 = _bf16(rng, (vocab, rank))
         W2 = _dev(w2.view(np.int16), torch.int16)
         W2c = torch.empty_like(W2)
         asv.markov_pack_w2(W2, vocab, rank, W2c)
         torch.cuda.synchronize()
-        want = w2.reshape(vocab, rank // 8, 8).transpose(1, 0, 2).reshape(-1)
+        want = np.concatenate([w2[t:t + 64].reshape(-1, rank // 8, 8).transpose(1, 0, 2).reshape(-1)
+                               for t in range(0, vocab, 64)])
         assert np.array_equal(W2c.cpu().numpy().view(np.uint16).reshape(-1), want)
 
 
