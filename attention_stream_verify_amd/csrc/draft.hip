@@ -1,9 +1,11 @@
 // Draft-id gather with a failure flag (gfx950).
 //
-// PR #1391 "lfm2: draft with LiquidAI's DSpark drafter (--drafter)": a kernel
-// copies each window's drafts from the drafter's picks into the verify's
-// ids, every pick exactly or 0 past the vocabulary, and sets a flag that the
-// verify reads before any cache commit when a pick is NaN, Inf or invalid.
+// PR #1391 "lfm2: draft with LiquidAI's DSpark drafter (--drafter)", its
+// description and the held-draft fix: a device kernel moves the drafter's
+// picks for every window into the id array the verify step consumes (a
+// token id past the vocabulary becomes 0), and raises a per-stream flag,
+// checked before the caches are committed, when a pick is invalid or came
+// from a row holding a NaN or an infinity.
 // The rule per entry is written out in include/asv_draft.h.
 //
 // One 256-thread block per stream: threads stride over the stream's span,

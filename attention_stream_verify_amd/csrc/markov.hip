@@ -1,10 +1,12 @@
 // Markov-head step of the drafter: each drafted row's pick from its logits
 // plus W2 . W1[previous token] (gfx950).
 //
-// PR #1391 "lfm2: draft with LiquidAI's DSpark drafter (--drafter)": the
-// Markov head adds W2 W1[previous token] to each block row's logits and
-// takes the argmax, one row after the other (ties to the lowest token, a NaN
-// score flagged); its testing notes write the score as
+// PR #1391 "lfm2: draft with LiquidAI's DSpark drafter (--drafter)",
+// description and new-kernel list: the drafter's Markov head scores a block
+// row as its logits plus W2 . W1[token before the row] and takes that row's
+// argmax before the next row, which uses the pick as its previous token
+// (lowest token on a tie, a NaN score flagged); its testing notes write the
+// score as
 // bf16(base + bf16(W2 . W1[prev])), at rows x vocabulary x rank
 // 1 x 128,000 x 256; the config admission caps the rank at 256. The exact
 // arithmetic (float32 dot, k ascending, one rounding per term) is written

@@ -1,9 +1,10 @@
 // Segment table of a shared round: host code, no HIP calls.
 //
 // PR #1377 "LFM2: shared-round decode", shared-round commit: each layer runs
-// once over every row of every live stream from a table of the streams'
-// cache addresses, row offsets and key counts; the table carries a row map
-// and tiles, and each stream's attention partials get a range of their own.
+// once over every row of every live stream, driven by one per-stream table
+// (where each stream's caches live, where its rows start, how many keys it
+// holds); the table carries a row map and tiles, and each stream's attention
+// partials get a range of their own.
 // The layout of every array is given in include/asv.h.
 
 #include <algorithm>

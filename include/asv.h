@@ -5,9 +5,9 @@
  * Where the operations come from (the pages' problem statement):
  *   PR #1377 "LFM2: shared-round decode" -- commit log and "What this
  *   changes": a shared round of several streams runs each layer's short conv
- *   and attention ONCE over all rows of all streams, through a table of the
- *   streams' cache addresses, row offsets and key counts, with each stream's
- *   attention partials held apart; a GPU argmax picks each head row's first
+ *   and attention ONCE over all rows of all streams, driven by one table
+ *   that says per stream where its caches live, where its rows start and how
+ *   many keys it holds, with each stream's attention partials held apart; a GPU argmax picks each head row's first
  *   largest logit and flags rows holding a nonfinite logit, so the host only
  *   draws flagged, sampled or masked rows.
  *
@@ -150,8 +150,8 @@ const char* asv_strerror(int code);
 
 /* Build the round's segment table on the host (no HIP call).
  *
- * Defines: PR #1377 "LFM2: shared-round decode", shared-round commit (a table
- * of the streams' cache addresses, row offsets and key counts; a row map and
+ * Defines: PR #1377 "LFM2: shared-round decode", shared-round commit (one
+ * per-stream table of cache addresses, first rows and key counts; a row map and
  * tiles; the partials of each stream kept apart, their count checked at 1,
  * 32 and 2,048 rows).
  *
@@ -205,9 +205,20 @@ int asv_block_table_build(const asv_stream_desc* streams, int32_t n_streams,
                           int32_t n_attn_layers, void* blob, size_t blob_bytes,
                           asv_table_info* info);
 
-/* Copy a built blob (host) to dev_blob (device, >= info->blob_bytes,
- * 16-byte aligned) on `stream`. The host blob must stay unchanged until the
- * copy has run (pinned host memory makes the copy asynchronous). */
+/* Copy a built blob (host) to the device, where every launch reads it.
+ *
+ * Defines: PR #1377 "LFM2: shared-round decode", shared-round commit (the
+ * round's table is written once on the host and read by every layer's
+ * launches on the GPU).
+ *
+ *   blob, bytes  host, the blob asv_seg_table_build or asv_block_table_build
+ *                wrote, bytes = info->blob_bytes; it must stay unchanged
+ *                until the copy has run (pinned host memory makes the copy
+ *                asynchronous)
+ *   dev_blob     device, >= bytes, 16-byte aligned; owned by the caller
+ * bytes == 0 copies nothing and returns ASV_OK.
+ * Errors: ASV_E_ARG (null blob or dev_blob, dev_blob not 16-byte aligned),
+ * ASV_E_HIP (the runtime refused the copy). */
 int asv_table_upload(const void* blob, size_t bytes, void* dev_blob, void* stream);
 
 /* Gated short conv of one layer over every row of the round.
@@ -295,6 +306,7 @@ size_t asv_row_argmax_workspace(int64_t rows, int64_t vocab);
 int asv_row_argmax(const uint16_t* logits, int64_t rows, int64_t vocab, int64_t row_stride,
                    int32_t* pick, uint8_t* flag, void* workspace, size_t workspace_bytes,
                    void* stream);
+
 
 #ifdef __cplusplus
 }

@@ -34,10 +34,11 @@ typedef struct {      /* one drafted block for asv_markov_pick             */
  * failure flag per stream.
  *
  * Defines: PR #1391 "lfm2: draft with LiquidAI's DSpark drafter
- * (--drafter)": a kernel copies each window's drafts from the drafter's
- * picks into the verify's ids, each pick exactly or 0 for a token past the
- * vocabulary; the held-draft fix adds a flag the verify reads before any
- * cache commit, so that a NaN, Inf or invalid pick fails (DraftNonfinite).
+ * (--drafter)", description: a device kernel moves the drafter's picks for
+ * every window into the id array the verify step consumes, an id past the
+ * vocabulary becoming 0; its held-draft fix: a per-stream flag, checked
+ * before the caches are committed, fails a window whose pick is invalid or
+ * came from a row with a NaN or an infinity (DraftNonfinite).
  *
  * For stream s (span = spans[s]) and i < span.count:
  *   p = pick[span.src + i];  ids[span.dst + i] = (0 <= p < vocab) ? p : 0
@@ -64,9 +65,11 @@ int asv_draft_ids(const asv_draft_span* spans, int32_t n_streams, const int32_t*
 /* Markov-head step of the drafter: each drafted row's pick and flag.
  *
  * Defines: PR #1391 "lfm2: draft with LiquidAI's DSpark drafter
- * (--drafter)": the Markov head adds W2 W1[previous token] to each block
- * row's logits and takes the argmax, one row after the other, ties to the
- * lowest token, a NaN score flagged; the testing notes give the score as
+ * (--drafter)", description and new-kernel list: the drafter's Markov head
+ * scores each row of the block as its logits plus the low-rank term
+ * W2 . W1[token before the row] and picks that row's argmax before it moves
+ * to the next row, whose previous token is that pick (lowest token on a
+ * tie, a NaN score flagged); the testing notes give the score as
  * bf16(base + bf16(W2 . W1[prev])) at 1 x 128,000 x 256 (rows x vocabulary
  * x rank); the config admission caps the rank at 256.
  *

@@ -1,11 +1,11 @@
 """Draft-id gather with a failure flag (oracle; test infrastructure only).
 
-PR #1391 "lfm2: draft with LiquidAI's DSpark drafter (--drafter)": a new
-kernel copies each window's drafts from the drafter's picks into the
-verify's ids, each pick copied exactly or 0 for a token past the
-vocabulary; after the fix for held drafts it also sets a flag that the
-verify reads before any cache commit, so that a NaN, Inf or invalid pick
-fails as the synchronous path does. Readings (listed in the design notes):
+PR #1391 "lfm2: draft with LiquidAI's DSpark drafter (--drafter)", its
+description and the held-draft fix: a new device kernel moves the drafter's
+picks for every window into the id array the verify step consumes, an id
+past the vocabulary becoming 0; after the fix it also raises a flag, checked
+before the caches are committed, so an invalid pick or one from a NaN or
+infinite row fails the same way as on the synchronous path. Readings (listed in the design notes):
 
 * a stream s is a span (src_s, dst_s, count_s): picks[src_s + i] goes to
   ids[dst_s + i] for i < count_s; ids outside the spans are not written;

@@ -2,9 +2,10 @@
 (oracle; test infrastructure only).
 
 PR #1391 "lfm2: draft with LiquidAI's DSpark drafter (--drafter)", its
-description and list of new kernels: the Markov head adds W2 W1[previous
-token] to each block row's logits and takes the argmax, one row after the
-other; the step kernels gather W1's row, take the W2 dot (bf16 weights by
+description and list of new kernels: the drafter's Markov head scores each
+row of the block as its logits plus W2 . W1[token before the row] and takes
+that row's argmax before the next row, which uses the pick as its previous
+token; the step kernels gather W1's row, take the W2 dot (bf16 weights by
 default: the bf16 scan), add it to the row's logits and pick the argmax,
 ties to the lowest token, a NaN score flagged. The PR's testing notes give
 the family test's rule, the argmax of bf16(base + bf16(W2 . W1[prev])), and

@@ -107,6 +107,33 @@ def sample_rows(table, n_extra, seed):
     return sorted(rows)
 
 
+def sample_rows_every_tile(table, n_extra, seed):
+    """Rows from every segment and every tile: the first, a middle and the
+    last row of each stream; for streams longer than one tile (prompt chunks)
+    the first row of every 16-row tile (the row that sees the fewest of the
+    tile's keys, where the causal mask cuts deepest into the tile's last
+    sub-blocks) and the last row of every fourth tile; plus n_extra seeded
+    random rows."""
+    rows = set()
+    for s in range(len(table.rows)):
+        a, b = int(table.seg_off[s]), int(table.seg_off[s + 1])
+        rows.update((a, (a + b - 1) // 2, b - 1))
+    for (s, row0, nrows, pos0) in table.tiles:
+        if table.rows[int(s)] > otable.TILE_ROWS:
+            rows.add(int(row0))
+            if (int(pos0) // otable.TILE_ROWS) % 4 == 3:
+                rows.add(int(row0) + int(nrows) - 1)
+    rng = np.random.default_rng(seed)
+    for r in rng.integers(0, table.n_rows, size=n_extra):
+        rows.add(int(r))
+    return sorted(rows)
+
+
+def chunk_rows(table, rows):
+    """The rows of `rows` that belong to streams longer than one tile."""
+    return [r for r in rows if table.rows[int(table.row_stream[r])] > otable.TILE_ROWS]
+
+
 def check_attention_layer(rnd, rb, partials, o_bits, li, rows, what, full=False):
     """Compare a layer's partials (every record of `rows`) and merged output."""
     t = otable.build(rnd.streams, full=full)

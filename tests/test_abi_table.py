@@ -139,13 +139,10 @@ def test_refusals_match_the_oracle(streams, code):
 def test_refuses_aliasing_and_misaligned_addresses():
     streams = [(1, 100, 128), (2, 100, 128)]
     _, _, _, (cs, kp, vp) = _build(streams)
-    # every stream reading the first stream's conv state / kv cache
-    for bad in ([[cs[0][0], cs[0][0]]], None):
-        if bad is None:
-            break
-        with pytest.raises(asv.AsvError) as e:
-            asv.seg_table_build(streams, bad, kp, vp)
-        assert e.value.code == -1
+    # every stream naming the first stream's conv state / kv cache
+    with pytest.raises(asv.AsvError) as e:
+        asv.seg_table_build(streams, [[cs[0][0], cs[0][0]]], kp, vp)
+    assert e.value.code == -1
     with pytest.raises(asv.AsvError) as e:
         asv.seg_table_build(streams, cs, [[kp[0][0], kp[0][0]]], vp)
     assert e.value.code == -1

@@ -16,7 +16,8 @@ from oracle import argmax as oargmax
 from oracle import conv as oconv
 from oracle import table as otable
 
-from helpers import (check_attention_layer, check_bf16_out, host_u16, run_round, sample_rows)
+from helpers import (check_attention_layer, check_bf16_out, chunk_rows, host_u16, run_round,
+                     sample_rows, sample_rows_every_tile)
 
 pytestmark = pytest.mark.gpu
 
@@ -198,19 +199,34 @@ def test_conv_window_equals_one_row_rounds():
 
 # ---------------------------------------------------------------- attention
 
-@pytest.mark.parametrize("config,extra", [(0, 0), (1, 8), (2, 8), (3, 6), (4, 10)])
-def test_attention_parity(config, extra):
+def _parity_rows(t, config):
+    """Every row of the tiny, decode, verify and long-context rounds; at 2,048
+    rows, rows from every segment and every 16-row tile of the prompt chunks."""
+    return list(range(t.n_rows)) if config != 4 else sample_rows_every_tile(t, 10, config)
+
+
+def _check_layer_by_part(rnd, rb, out, t, rows, what, full=False):
+    """Check window rows and prompt-chunk rows apart and print both."""
+    chunk = chunk_rows(t, rows)
+    window = [r for r in rows if r not in set(chunk)]
+    for part, rr in (("window", window), ("chunk", chunk)):
+        if not rr:
+            continue
+        prel, oerr = check_attention_layer(rnd, rb, out["partials"][0], out["o"][0], 0, rr,
+                                           f"{what} {part} rows", full=full)
+        print(f"[parity] {what}: {len(rr)} {part} rows (keys {int(t.row_nkeys[rr].min())}-"
+              f"{int(t.row_nkeys[rr].max())}), partial o rel err {prel:.2e}, "
+              f"output abs err {oerr:.2e}", flush=True)
+        if part == "chunk":
+            print(f"[parity] {what}: chunk rows checked {rr}", flush=True)
+
+
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+def test_attention_parity(config):
     rnd = _round(config, n_conv=0, n_attn=1, with_logits=False)
     rb, out = run_round(rnd, with_argmax=False)
     t = otable.build(rnd.streams)
-    rows = list(range(t.n_rows)) if config == 0 else sample_rows(t, extra, config)
-    if config == 4:
-        rows = [r for r in rows if t.row_nkeys[r] <= 40000][:40] + \
-               [r for r in rows if t.row_nkeys[r] > 40000][:4]
-    prel, oerr = check_attention_layer(rnd, rb, out["partials"][0], out["o"][0], 0, rows,
-                                       f"attn {config}")
-    print(f"[parity] workload {config}: {len(rows)} rows, partial o rel err {prel:.2e}, "
-          f"output abs err {oerr:.2e}", flush=True)
+    _check_layer_by_part(rnd, rb, out, t, _parity_rows(t, config), f"attn {config}")
 
 
 @pytest.mark.parametrize("streams", [
@@ -320,19 +336,12 @@ def test_isolation_by_perturbation_and_determinism():
 # Tables from asv_block_table_build: every row sees all of its stream's keys
 # (PR #1391's FULL block attention); same kernels, same bounds.
 
-@pytest.mark.parametrize("config,extra", [(0, 0), (2, 8), (3, 6), (4, 10)])
-def test_block_attention_parity(config, extra):
+@pytest.mark.parametrize("config", [0, 2, 3, 4])
+def test_block_attention_parity(config):
     rnd = _round(config, n_conv=0, n_attn=1, with_logits=False)
     rb, out = run_round(rnd, with_argmax=False, full=True)
     t = otable.build(rnd.streams, full=True)
-    rows = list(range(t.n_rows)) if config == 0 else sample_rows(t, extra, config)
-    if config == 4:
-        rows = [r for r in rows if t.row_nkeys[r] <= 40000][:40] + \
-               [r for r in rows if t.row_nkeys[r] > 40000][:4]
-    prel, oerr = check_attention_layer(rnd, rb, out["partials"][0], out["o"][0], 0, rows,
-                                       f"block {config}", full=True)
-    print(f"[parity] block workload {config}: {len(rows)} rows, partial o rel err {prel:.2e}, "
-          f"output abs err {oerr:.2e}", flush=True)
+    _check_layer_by_part(rnd, rb, out, t, _parity_rows(t, config), f"block {config}", full=True)
 
 
 @pytest.mark.parametrize("streams", [

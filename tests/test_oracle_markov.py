@@ -1,7 +1,7 @@
-"""Pins of the Markov-step oracle (PR #1391: the Markov head adds
-W2 W1[previous token] to each row's logits and takes the argmax, one row
-after the other; ties to the lowest token; a NaN score flagged; the testing
-notes' rule bf16(base + bf16(W2 . W1[prev]))).
+"""Pins of the Markov-step oracle (PR #1391, description: each drafted row
+is scored as its logits plus W2 . W1[token before the row], rows taken in
+order with each pick feeding the next row; lowest token on a tie; a NaN
+score flagged; the testing notes' rule bf16(base + bf16(W2 . W1[prev]))).
 
 Pinned against: a hand-derived accumulation-order fixture, integer weights
 (the dot exact in any order) with torch's own bf16 rounding for the two
