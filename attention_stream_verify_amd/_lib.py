@@ -34,7 +34,8 @@ SYMBOLS = [
     "asv_abi_version", "asv_strerror", "asv_seg_table_build", "asv_block_table_build",
     "asv_table_upload",
     "asv_shared_conv", "asv_shared_attn", "asv_attn_merge", "asv_row_argmax_workspace",
-    "asv_row_argmax", "asv_draft_ids", "asv_markov_workspace", "asv_markov_pick",
+    "asv_row_argmax", "asv_row_argmax_noalloc", "asv_draft_ids", "asv_markov_workspace",
+    "asv_markov_pick",
     "asv_markov_pack_w2", "asv_shared_qk",
 ]
 
@@ -115,6 +116,8 @@ def lib():
         L.asv_row_argmax_workspace.argtypes = [i64, i64]
         L.asv_row_argmax.restype = ctypes.c_int
         L.asv_row_argmax.argtypes = [vp, i64, i64, i64, vp, vp, vp, sz, vp]
+        L.asv_row_argmax_noalloc.restype = ctypes.c_int
+        L.asv_row_argmax_noalloc.argtypes = [vp, i64, i64, i64, vp, vp, vp]
         L.asv_draft_ids.restype = ctypes.c_int
         L.asv_draft_ids.argtypes = [vp, i32, vp, vp, i64, i64, vp, i64, vp, vp]
         L.asv_markov_workspace.restype = sz
@@ -277,6 +280,17 @@ def row_argmax(logits, rows, vocab, row_stride, pick, flag, workspace, stream=No
     _check(lib().asv_row_argmax(_addr(logits), int(rows), int(vocab), int(row_stride), _addr(pick),
                                 _addr(flag), _addr(workspace), nbytes, _stream(stream)),
            "asv_row_argmax")
+
+
+ARGMAX_SCRATCH_BYTES = 4 << 20
+
+
+def row_argmax_noalloc(logits, rows, vocab, row_stride, pick, flag, stream=None):
+    """asv_row_argmax_noalloc: the same picks and flags, the workspace being
+    the library's own device array (no allocation)."""
+    _check(lib().asv_row_argmax_noalloc(_addr(logits), int(rows), int(vocab), int(row_stride),
+                                        _addr(pick), _addr(flag), _stream(stream)),
+           "asv_row_argmax_noalloc")
 
 
 def draft_ids(spans, n_streams, pick, pick_flag, n_picks, vocab, ids, n_ids, fail, stream=None):

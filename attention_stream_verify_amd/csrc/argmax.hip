@@ -15,8 +15,16 @@
 // a handful of CUs. The result is exact, so the chunking never changes it.
 
 #include <climits>
+#include <mutex>
 
 #include "device.h"
+
+// Library-owned workspace of asv_row_argmax_noalloc: one array per GPU, in
+// the code object's device memory, held until the process ends. Every chunk
+// record is written by argmax_chunks before argmax_rows reads it, so nothing
+// in it needs clearing between calls.
+static_assert(ASV_ARGMAX_SCRATCH_BYTES % sizeof(int4) == 0, "scratch size");
+static __device__ __align__(256) int4 scratch[ASV_ARGMAX_SCRATCH_BYTES / sizeof(int4)];
 
 namespace asv {
 namespace {
@@ -131,6 +139,53 @@ __global__ __launch_bounds__(256) void argmax_rows(const int4* __restrict__ ws, 
 
 int chunks_for(int64_t vocab) { return int((vocab + kChunk - 1) / kChunk); }
 
+// Argument checks shared by both entry points; the workspace is checked by
+// each caller.
+int check_args(const uint16_t* logits, int64_t rows, int64_t vocab, int64_t row_stride,
+               const int32_t* pick, const uint8_t* flag) {
+  if (rows < 0 || vocab < 1 || vocab > (int64_t(1) << 30) || row_stride < vocab)
+    return ASV_E_SHAPE;
+  if (rows == 0) return ASV_OK;
+  if (logits == nullptr || pick == nullptr || flag == nullptr) return ASV_E_ARG;
+  if (!aligned16(logits) || row_stride % 8 != 0) return ASV_E_ARG;
+  if (rows * int64_t(chunks_for(vocab)) > int64_t(INT_MAX)) return ASV_E_SHAPE;
+  return ASV_OK;
+}
+
+// The two launches over a workspace of rows x chunks records.
+int launch(const uint16_t* logits, int64_t rows, int64_t vocab, int64_t row_stride,
+           int32_t* pick, uint8_t* flag, int4* ws, hipStream_t st) {
+  const int nchunk = chunks_for(vocab);
+  hipLaunchKernelGGL(argmax_chunks, dim3(unsigned(rows * nchunk)), dim3(kThreads), 0, st,
+                     logits, vocab, row_stride, nchunk, ws);
+  if (hipGetLastError() != hipSuccess) return ASV_E_HIP;
+  hipLaunchKernelGGL(argmax_rows, dim3(unsigned((rows + 255) / 256)), dim3(256), 0, st, ws, rows,
+                     nchunk, pick, flag);
+  if (hipGetLastError() != hipSuccess) return ASV_E_HIP;
+  return ASV_OK;
+}
+
+// The array's device address, resolved once per device with that device
+// current. On the host, `scratch` names a host-side stand-in, never the
+// device memory, so it is only ever used through these addresses.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(int4** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ASV_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(::scratch)) != hipSuccess || p == nullptr)
+      return ASV_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<int4*>(g_scratch_ptr[dev]);
+  return ASV_OK;
+}
+
 }  // namespace
 }  // namespace asv
 
@@ -142,23 +197,23 @@ extern "C" size_t asv_row_argmax_workspace(int64_t rows, int64_t vocab) {
 extern "C" int asv_row_argmax(const uint16_t* logits, int64_t rows, int64_t vocab,
                               int64_t row_stride, int32_t* pick, uint8_t* flag, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  if (rows < 0 || vocab < 1 || vocab > (int64_t(1) << 30) || row_stride < vocab)
-    return ASV_E_SHAPE;
-  if (rows == 0) return ASV_OK;
-  if (logits == nullptr || pick == nullptr || flag == nullptr || workspace == nullptr)
-    return ASV_E_ARG;
-  if (!asv::aligned16(logits) || !asv::aligned16(workspace) || row_stride % 8 != 0)
-    return ASV_E_ARG;
-  const int nchunk = asv::chunks_for(vocab);
-  if (rows * int64_t(nchunk) > int64_t(INT_MAX)) return ASV_E_SHAPE;
+  const int e = asv::check_args(logits, rows, vocab, row_stride, pick, flag);
+  if (e != ASV_OK || rows == 0) return e;
+  if (workspace == nullptr || !asv::aligned16(workspace)) return ASV_E_ARG;
   if (workspace_bytes < asv_row_argmax_workspace(rows, vocab)) return ASV_E_CAPACITY;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  int4* ws = static_cast<int4*>(workspace);
-  hipLaunchKernelGGL(asv::argmax_chunks, dim3(unsigned(rows * nchunk)), dim3(asv::kThreads), 0,
-                     st, logits, vocab, row_stride, nchunk, ws);
-  if (hipGetLastError() != hipSuccess) return ASV_E_HIP;
-  hipLaunchKernelGGL(asv::argmax_rows, dim3(unsigned((rows + 255) / 256)), dim3(256), 0, st, ws,
-                     rows, nchunk, pick, flag);
-  if (hipGetLastError() != hipSuccess) return ASV_E_HIP;
-  return ASV_OK;
+  return asv::launch(logits, rows, vocab, row_stride, pick, flag, static_cast<int4*>(workspace),
+                     static_cast<hipStream_t>(stream));
+}
+
+extern "C" int asv_row_argmax_noalloc(const uint16_t* logits, int64_t rows, int64_t vocab,
+                                      int64_t row_stride, int32_t* pick, uint8_t* flag,
+                                      void* stream) {
+  const int e = asv::check_args(logits, rows, vocab, row_stride, pick, flag);
+  if (e != ASV_OK || rows == 0) return e;
+  if (asv_row_argmax_workspace(rows, vocab) > size_t(ASV_ARGMAX_SCRATCH_BYTES)) return ASV_E_CAPACITY;
+  int4* ws = nullptr;
+  const int se = asv::scratch_for_current_device(&ws);
+  if (se != ASV_OK) return se;
+  return asv::launch(logits, rows, vocab, row_stride, pick, flag, ws,
+                     static_cast<hipStream_t>(stream));
 }

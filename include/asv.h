@@ -307,6 +307,34 @@ int asv_row_argmax(const uint16_t* logits, int64_t rows, int64_t vocab, int64_t 
                    int32_t* pick, uint8_t* flag, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Bytes of the device array asv_row_argmax_noalloc uses as its workspace. */
+#define ASV_ARGMAX_SCRATCH_BYTES (4u << 20)
+
+/* asv_row_argmax without a caller workspace and without any allocation.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same pick,
+ * flag, arguments (minus the workspace), layout and results as
+ * asv_row_argmax, bit for bit; the two launches are the same kernels.
+ *
+ * Workspace: a library-owned device array of ASV_ARGMAX_SCRATCH_BYTES
+ * (4 MiB) on each GPU the library runs on, held until the process ends;
+ * its address is resolved on the first call on a device (no allocation,
+ * no copy). So asv_row_argmax_workspace(rows, vocab) must not exceed 4 MiB:
+ * rows * ceil(vocab / 8192) <= 262,144 (e.g. 2,048 rows of up to 1,048,576
+ * logits, or 16,384 rows of 128,000). Nothing in the array needs clearing:
+ * every record is written before it is read.
+ *
+ * Every call on one GPU shares that GPU's array: calls whose work overlaps
+ * in time on one GPU (on two streams, or from two host threads without
+ * ordering) race on it and give undefined picks. Calls on one stream, one
+ * after the other, are safe.
+ *
+ * Errors: those of asv_row_argmax; ASV_E_CAPACITY when the workspace the
+ * call needs exceeds ASV_ARGMAX_SCRATCH_BYTES; ASV_E_HIP when the array's
+ * device address cannot be resolved. rows == 0 launches nothing. */
+int asv_row_argmax_noalloc(const uint16_t* logits, int64_t rows, int64_t vocab,
+                           int64_t row_stride, int32_t* pick, uint8_t* flag, void* stream);
 
 #ifdef __cplusplus
 }
