@@ -13,8 +13,12 @@ it runs on, against 8 TB/s); attention + merge per layer (K/V + Q + O bytes
 over the pair's time; alternate rounds time the pair with no event between
 the two kernels and the attention alone); the profiled HBM traffic and MFMA
 busy fraction when profiles/ holds them for these kernel sources; the host
-table build time; and the CPU oracle timed on a bounded sample of the same
-workload.
+table build time; the CPU oracle timed on a bounded sample of the same
+workload; and a per-workload object: every workload (tiny, 16 x 1 decode,
+16 x 8 verify, 4 x 16 long context, the 2,048-row scratch) measured in the
+same run the same way -- rows/s, round time, the attention launch against
+8 TB/s and against its max(bytes / 8 TB/s, flops / 2.5 PFLOP/s) bound, and
+the attention + merge pair.
 """
 
 import argparse
@@ -45,6 +49,10 @@ def parse():
     p.add_argument("--config", type=int, default=3, choices=[0, 1, 2, 3, 4])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-markov", action="store_true", help="skip the Markov-head timing leg")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="skip the per-workload object (every workload's round, measured in this run)")
+    p.add_argument("--workload-steps", type=int, default=10,
+                   help="timed rounds of each workload of the per-workload object")
     p.add_argument("--eager", action="store_true",
                    help="time the rounds as eager launches (default: replays of one captured HIP graph)")
     p.add_argument("--with-qk", action="store_true",
@@ -70,6 +78,10 @@ def calibrate_copy(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n, "reads": n, "writes": n}), flush=True)
+
+
+WORKLOAD_KEYS = {0: "tiny", 1: "decode_16x1", 2: "verify_16x8", 3: "long_context_4x16",
+                 4: "scratch_2048"}
 
 
 TRAFFIC_PROFILES = {3: "profiles/attn_split_long_context_traffic.md"}
@@ -222,6 +234,134 @@ def markov_leg(torch, asv, dev, seed, calls=20):
             "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
+def measure_round(torch, asv, workloads, dev, config, steps, warmup, block=False, with_qk=False,
+                  eager=False, seed=None):
+    """Build one workload's inputs and time its rounds.
+
+    Eager rounds (events on torch's current stream, the stream the library
+    launches on) give the per-kernel times: odd rounds record events around
+    each attention launch alone, even rounds around each attention + merge
+    pair (no event between the two kernels). Then, unless eager, the round is
+    captured once as a HIP graph (the table upload and every launch) and
+    replayed: ``ms_step`` is the replays' time per round, the same work with
+    the host's per-launch cost taken out. Returns the measurements and the
+    objects the other legs reuse."""
+    rnd = workloads.Round(config, device=dev, seed=seed)
+    R, S = rnd.R, rnd.S
+    rb = asv.RoundBuffers(rnd.streams, [layer[2] for layer in rnd.conv],
+                          [layer[1] for layer in rnd.attn], [layer[2] for layer in rnd.attn],
+                          device=dev, vocab=rnd.logits.shape[1], full=block)
+    order = layer_order(rnd.n_conv, rnd.n_attn)
+    sum_keys = sum(k for _, k, _ in rnd.streams)
+    attn_bytes = 2048 * sum_keys + 4096 * R            # K/V once + Q, per launch
+    # algorithmic attention flops a launch: q.k and p.v, 2 * 64 multiply-adds
+    # each, for every (row, q head, visible key)
+    visible = sum((k if block else k - w + i + 1) for w, k, _ in rnd.streams for i in range(w))
+    attn_flops = 4 * 64 * 32 * visible
+    merge_bytes = 4096 * R                              # O written (partials are a means)
+    qkv, gq, gk = workloads.qk_inputs(R, seed=rnd.seed + 7, device=dev)
+
+    def event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def step(ev=None, split=False):
+        """One round; with ev, events: round start, per attention layer
+        (start, end of the attention alone when split, else of the pair),
+        round end."""
+        if ev is not None:
+            ev.append([event()])
+        rb.upload()
+        for kind, i in order:
+            if kind == "conv":
+                X, W, _ = rnd.conv[i]
+                rb.conv(i, X, W)
+            else:
+                if with_qk:
+                    rb.qk(i, qkv, gq, gk, workloads.ROPE_THETA, workloads.NORM_EPS)
+                if ev is not None:
+                    ev[-1].append(event())
+                rb.attn(i, rb.q if with_qk else rnd.attn[i][0])
+                if ev is not None and split:
+                    ev[-1].append(event())
+                rb.merge()
+                if ev is not None and not split:
+                    ev[-1].append(event())
+        rb.argmax(rnd.logits)
+        if ev is not None:
+            ev[-1].append(event())
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = []
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(steps):
+        step(ev, split=(k % 2 == 1))
+    stop.record()
+    torch.cuda.synchronize()
+    eager_ms_step = start.elapsed_time(stop) / steps
+    round_ms = sorted(e[0].elapsed_time(e[-1]) for e in ev)
+    attn_ms, pair_ms = [], []
+    for k, e in enumerate(ev):
+        for j in range(1, len(e) - 1, 2):
+            (attn_ms if k % 2 == 1 else pair_ms).append(e[j].elapsed_time(e[j + 1]))
+    if not attn_ms:  # a single timed round: time attention alone in it
+        attn_ms = pair_ms
+    ms_step = eager_ms_step
+    if not eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_step = g0.elapsed_time(g1) / steps
+        del graph
+    return {
+        "rnd": rnd, "rb": rb, "R": R, "S": S, "sum_keys": sum_keys, "attn_bytes": attn_bytes,
+        "attn_flops": attn_flops, "merge_bytes": merge_bytes, "qkv": (qkv, gq, gk),
+        "ms_step": ms_step, "eager_ms_step": eager_ms_step, "round_ms": round_ms,
+        "attn_us": sum(attn_ms) / len(attn_ms) * 1e3, "pair_us": sum(pair_ms) / len(pair_ms) * 1e3,
+    }
+
+
+def pct(xs, q):
+    return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+
+
+def attn_bound_us(m):
+    """max(bytes / HBM peak, flops / bf16 MFMA peak) of one attention launch."""
+    return max(m["attn_bytes"] / (HBM_PEAK_GBS * 1e3), m["attn_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e6))
+
+
+def workload_entry(m):
+    """One workload of the per-workload object: round time, rows/s, the
+    attention launch against its HBM roofline and its max(bytes/BW,
+    flops/peak) bound, and the attention + merge pair."""
+    a_gbs = m["attn_bytes"] / (m["attn_us"] * 1e-6) / 1e9
+    pair_bytes = m["attn_bytes"] + m["merge_bytes"]
+    bound = attn_bound_us(m)
+    return {
+        "rows": m["R"], "streams": m["S"], "sum_keys": m["sum_keys"],
+        "rows_per_s": m["R"] / (m["ms_step"] * 1e-3), "round_ms": m["ms_step"],
+        "eager_round_ms_median": m["round_ms"][len(m["round_ms"]) // 2],
+        "attn_us": m["attn_us"], "attn_gbs": a_gbs, "attn_frac_hbm": a_gbs / HBM_PEAK_GBS,
+        "attn_flops": m["attn_flops"], "attn_bound_us": bound, "attn_frac_of_bound": bound / m["attn_us"],
+        "attn_merge_us": m["pair_us"],
+        "attn_merge_frac_hbm": pair_bytes / (m["pair_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -241,103 +381,14 @@ def main():
     asv.lib()  # fails loudly when libasv.so is missing
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    rnd = workloads.Round(args.config, device=dev, seed=args.seed)
-    R, S = rnd.R, rnd.S
-    rb = asv.RoundBuffers(rnd.streams, [layer[2] for layer in rnd.conv],
-                          [layer[1] for layer in rnd.attn], [layer[2] for layer in rnd.attn],
-                          device=dev, vocab=rnd.logits.shape[1], full=args.block)
-    order = layer_order(rnd.n_conv, rnd.n_attn)
-    sum_keys = sum(k for _, k, _ in rnd.streams)
-    attn_bytes = 2048 * sum_keys + 4096 * R            # K/V once + Q, per launch
-    # algorithmic attention flops a launch: q.k and p.v, 2 * 64 multiply-adds
-    # each, for every (row, q head, visible key)
-    visible = sum((k if args.block else k - w + i + 1) for w, k, _ in rnd.streams for i in range(w))
-    attn_flops = 4 * 64 * 32 * visible
-    merge_bytes = 4096 * R                              # O written (partials are a means)
-
-    def event():
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
-
-    qkv, gq, gk = workloads.qk_inputs(R, seed=rnd.seed + 7, device=dev)
-    qk_bytes = R * (2 * 3072 + 2 * 2048 + 2 * 512 + 2 * 512) + 2 * 128   # qkv in; q, k, v out; gains
-
-    def step(ev=None, split=False):
-        """One round. With ev, records events on torch's current stream (the
-        stream the library launches on): round start, then per attention
-        layer either (attention start, attention end) when split, or
-        (attention start, merge end) -- no event between the two kernels --
-        and the round end."""
-        if ev is not None:
-            ev.append([event()])
-        rb.upload()
-        for kind, i in order:
-            if kind == "conv":
-                X, W, _ = rnd.conv[i]
-                rb.conv(i, X, W)
-            else:
-                if args.with_qk:
-                    rb.qk(i, qkv, gq, gk, workloads.ROPE_THETA, workloads.NORM_EPS)
-                if ev is not None:
-                    ev[-1].append(event())
-                rb.attn(i, rb.q if args.with_qk else rnd.attn[i][0])
-                if ev is not None and split:
-                    ev[-1].append(event())
-                rb.merge()
-                if ev is not None and not split:
-                    ev[-1].append(event())
-        rb.argmax(rnd.logits)
-        if ev is not None:
-            ev[-1].append(event())
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    ev = []
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for k in range(args.steps):
-        step(ev, split=(k % 2 == 1))
-    stop.record()
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / args.steps
-    round_ms = sorted(e[0].elapsed_time(e[-1]) for e in ev)
-    attn_ms, pair_ms = [], []
-    for k, e in enumerate(ev):
-        for j in range(1, len(e) - 1, 2):
-            (attn_ms if k % 2 == 1 else pair_ms).append(e[j].elapsed_time(e[j + 1]))
-    if not attn_ms:  # a single timed round: time attention alone in it
-        attn_ms = pair_ms
-    attn_avg_ms = sum(attn_ms) / len(attn_ms)
-    pair_avg_ms = sum(pair_ms) / len(pair_ms)
+    m = measure_round(torch, asv, workloads, dev, args.config, args.steps, args.warmup,
+                      block=args.block, with_qk=args.with_qk, eager=args.eager, seed=args.seed)
+    rnd, rb, R, S = m["rnd"], m["rb"], m["R"], m["S"]
+    attn_bytes, attn_flops, merge_bytes = m["attn_bytes"], m["attn_flops"], m["merge_bytes"]
+    attn_avg_ms, pair_avg_ms = m["attn_us"] * 1e-3, m["pair_us"] * 1e-3
     achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
-
-    def pct(xs, q):
-        return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
-
-    # The round as one captured HIP graph (the table upload and every
-    # launch, on the capture stream), replayed W times untimed and K times
-    # timed: the same work with the host's per-launch cost taken out. The
-    # eager rounds above stay the source of the per-kernel event timings.
-    eager_ms_step = ms_step
-    if not args.eager:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record()
-        for _ in range(args.steps):
-            graph.replay()
-        g1.record()
-        torch.cuda.synchronize()
-        ms_step = g0.elapsed_time(g1) / args.steps
+    qkv, gq, gk = m["qkv"]
+    round_ms = m["round_ms"]
 
     # draft-id gather over the round's picks, queued behind an attention
     # launch like the qk leg below, so the events time the kernels
@@ -379,12 +430,12 @@ def main():
         "metric": ("verify rows/sec per shared round (conv+qk+attn+argmax); attn HBM GB/s vs peak"
                    if args.with_qk else
                    "verify rows/sec per shared round (conv+attn+argmax); attn HBM GB/s vs peak"),
-        "value": R / (ms_step * 1e-3),
+        "value": R / (m["ms_step"] * 1e-3),
         "unit": "rows/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": m["ms_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -396,7 +447,7 @@ def main():
                         + (", qk stage before every attention layer" if args.with_qk else ""),
             "streams": S,
             "rows": R,
-            "sum_keys": sum_keys,
+            "sum_keys": m["sum_keys"],
             "conv_layers": rnd.n_conv,
             "attn_layers": rnd.n_attn,
             "vocab": int(rnd.logits.shape[1]),
@@ -416,7 +467,7 @@ def main():
             "avg_launch_us": attn_avg_ms * 1e3,
         },
         "launch": "eager" if args.eager else "hip graph of one round",
-        "eager_ms_per_step": eager_ms_step,
+        "eager_ms_per_step": m["eager_ms_step"],
         "round_ms": {"median": round_ms[len(round_ms) // 2], "p10": pct(round_ms, 0.1),
                      "p90": pct(round_ms, 0.9)},
         "attn_merge": {
@@ -429,13 +480,36 @@ def main():
         "table_build_host_us": build_us,
         "draft_ids_us": draft_us,
         "markov": markov,
-        "qk": {"avg_launch_us": qk_avg, "bytes_per_launch": qk_bytes,
-               "achieved_gbs": qk_bytes / (qk_avg * 1e-6) / 1e9, "in_round": bool(args.with_qk)},
+        "qk": {"avg_launch_us": qk_avg, "bytes_per_launch": R * (2 * 3072 + 2 * 2048 + 2 * 512 + 2 * 512) + 2 * 128,
+               "achieved_gbs": (R * (2 * 3072 + 2 * 2048 + 2 * 512 + 2 * 512) + 2 * 128) / (qk_avg * 1e-6) / 1e9,
+               "in_round": bool(args.with_qk)},
+        "workloads": None,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(rnd, R, full=args.block)
         line["cpu_baseline"]["gpu_over_cpu"] = line["value"] / line["cpu_baseline"]["value"]
+
+    # every workload, measured in this run the same way (the default
+    # workload's own numbers are reused for its entry)
+    if not args.no_workloads:
+        entries = {}
+        del rnd, rb
+        m_self = workload_entry(m)
+        m_self.update({"mfma_busy": line["mfma_busy"]})
+        del m
+        for c in range(5):
+            if c == args.config and not args.block and not args.with_qk:
+                entries[WORKLOAD_KEYS[c]] = m_self
+                continue
+            mc = measure_round(torch, asv, workloads, dev, c, args.workload_steps, args.warmup,
+                               block=args.block, with_qk=args.with_qk, eager=args.eager)
+            e = workload_entry(mc)
+            e["mfma_busy"] = None if args.block else profiled_mfma(c)
+            entries[WORKLOAD_KEYS[c]] = e
+            del mc
+            torch.cuda.empty_cache()
+        line["workloads"] = entries
     print(json.dumps(line), flush=True)
 
 
