@@ -10,11 +10,10 @@
 // Work item = (16-row tile, kv head, split), one 256-thread block each. A
 // tile's q vectors are its rows x the 4 q heads of the kv head (up to 64),
 // in column tiles of 16. Every wave of the block holds all of the tile's q
-// tiles and streams its own quarter of the split's keys (32-key sub-blocks
-// w, w+4, ...) through a private LDS ring that direct global->LDS loads
-// fill; at the end the four waves fold their states through LDS in wave
-// order. Tiles of 13-16 rows keep their Q operands in LDS, read per q tile,
-// so that the four q tiles' accumulators fit in registers.
+// tiles (their Q operands in registers) and streams its own quarter of the
+// split's keys (32-key sub-blocks w, w+4, ...) through a private LDS ring
+// that direct global->LDS loads fill; at the end the four waves fold their
+// states through LDS in wave order.
 //
 // Per 32-key sub-block, on the bf16 16x16x32 MFMA (fp32 accumulate):
 //   S^T[key][q]  = K[key][:] . Q[q][:]        (2 key tiles x 2 d-steps)
@@ -59,23 +58,21 @@ __device__ __forceinline__ uint32_t zero_past(uint32_t w, int key, int keys) {
 
 // Per-wave online-softmax state for QPW q tiles. Per q column the wave
 // keeps an exponent base mref (raw score units; -inf until the column has
-// seen a key) and nmc = -mref*c, the sum l of its weights at that base, and
-// pm, the bits of the largest weight so far (weights are >= 0, so their
-// bits order as unsigned integers). A sub-block's weights are computed at
-// the current base straight away; only when one of them exceeds 2^kLazy
-// (a score more than kLazy/c above the base) does the wave take the rebase
-// path, which moves the base to the column max and rescales. So the common
-// path has no max reduction at all, and the accumulators are rescaled
-// rarely. At the end the true max follows from the largest weight:
-// mtrue = mref + log2(pm)/c, and l at the true max is l / pm.
+// seen a key), nmc = -mref*c, the sum l of its weights at that base, the
+// largest score ms it has seen, and thr = mref + kLazy/c. A sub-block's
+// scores are tested against thr first; only when one of them exceeds it (a
+// weight above 2^kLazy at the current base), or on the wave's first
+// sub-block, does the wave take the rebase path, which moves the bases to
+// the columns' max scores and rescales. So the common path has no cross-lane
+// max at all, and the accumulators are rescaled rarely. At the end the true
+// max is the largest score seen, and l is taken to it.
 template <int QPW>
 struct WaveState {
   f32x4 acc[4][QPW];
-  float mref[QPW], nmc[QPW], mtrue[QPW], l[QPW];
-  uint32_t pm[QPW];
+  float mref[QPW], nmc[QPW], thr[QPW], ms[QPW], l[QPW];
 };
 
-constexpr uint32_t kLazyBits = 0x43800000u;  // 256.0f: weights stay <= 2^8
+constexpr float kLazy = 8.f;  // weights stay <= 2^8 between rebases
 
 // Each wave streams its own 32-key sub-blocks (the item's sub-blocks w,
 // w+4, w+8, ... for wave w) through a private two-slot LDS ring filled by
@@ -153,59 +150,38 @@ __device__ __forceinline__ void issue_sub(char* slot, const uint16_t* __restrict
   lds_dma16<AUX, 3072>(vbase, voff, slot + 4096);
 }
 
-// Wide tiles keep their Q operands in LDS (read per q tile) rather than in
-// 32 registers, which a wave holding four q tiles cannot spare.
-template <int QPW>
-constexpr bool q_in_lds() { return QPW >= 4; }
-
-__device__ __forceinline__ uint32_t umax3(uint32_t a, uint32_t b, uint32_t c) {
-  return a > b ? (a > c ? a : c) : (b > c ? b : c);
-}
-
-// Weights of one q tile's 8 scores at base -nmc/c, and the bits of the largest.
-__device__ __forceinline__ uint32_t weights(const float (&sc)[8], float nmc, float (&p)[8]) {
-  const float c = kScale * kLog2e;
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) p[jj] = exp2_(__builtin_fmaf(sc[jj], c, nmc));
-  const uint32_t m0 = umax3(__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]));
-  const uint32_t m1 = umax3(__float_as_uint(p[3]), __float_as_uint(p[4]), __float_as_uint(p[5]));
-  return umax3(m0, m1, umax3(__float_as_uint(p[6]), __float_as_uint(p[7]), 0u));
-}
-
-// Does any weight of these 8 scores exceed 2^kLazy at base -nmc/c?
-__device__ __forceinline__ bool weights_over(const float (&sc)[8], float nmc) {
-  float p[8];
-  return weights(sc, nmc, p) > kLazyBits;
+// Max of three scores on gfx950's v_maximum3_f32 (a NaN propagates). fmaxf
+// would first quiet every MFMA result with an extra v_max_f32 x, x.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
 // Rebase q tile u (wave-uniform, rare): every column moves its base up to
-// its max so far; x * 1.0f leaves the bits of columns that do not move
-// unchanged.
+// its max score so far (smax: the lane's max of this sub-block); x * 1.0f
+// leaves the bits of columns that do not move unchanged.
 template <int QPW>
-__device__ __forceinline__ void rebase(WaveState<QPW>& st, int u, const float (&sc)[8]) {
+__device__ __forceinline__ void rebase(WaveState<QPW>& st, int u, float smax) {
   const float c = kScale * kLog2e;
   const float ninf = -__builtin_inff();
-  float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                   fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-  mx = max_xor32(max_xor16(mx));
+  const float mx = max_xor32(max_xor16(smax));
   const float mn = fmaxf(st.mref[u], mx);
   const float alpha = (mn > st.mref[u]) ? exp2_((st.mref[u] - mn) * c) : 1.f;
   st.mref[u] = mn;
   st.nmc[u] = (mn == ninf) ? 0.f : -mn * c;
+  st.thr[u] = mn + kLazy / c;
   st.l[u] *= alpha;
-  st.pm[u] = __float_as_uint(__uint_as_float(st.pm[u]) * alpha);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) st.acc[dt][u] *= alpha;
 }
 
-// Weights of q tile u's 8 scores at the current base into l, pm and, as
-// bf16 hi + lo, through the PV MFMAs into the accumulators.
+// q tile u's scores (in place: their weights at the current base) into l
+// and, as bf16 hi + lo, through the PV MFMAs into the accumulators.
 template <int QPW>
-__device__ __forceinline__ void accumulate(WaveState<QPW>& st, int u, const float (&sc)[8],
+__device__ __forceinline__ void accumulate(WaveState<QPW>& st, int u, float (&p)[8],
                                            const u32x4 (&v)[4]) {
-  float p[8];
-  const uint32_t pmax = weights(sc, st.nmc[u], p);
-  st.pm[u] = st.pm[u] > pmax ? st.pm[u] : pmax;
+  const float c = kScale * kLog2e;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) p[jj] = exp2_(__builtin_fmaf(p[jj], c, st.nmc[u]));
   st.l[u] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   u32x4 hi, lo;
 #pragma unroll
@@ -225,28 +201,66 @@ __device__ __forceinline__ void accumulate(WaveState<QPW>& st, int u, const floa
   }
 }
 
-// One 32-key sub-block for QPW q tiles; K/V operands come from the wave's
-// slot, Q operands from registers or (wide tiles) from the block's Q area.
-// EDGE: the sub-block reaches past some row's causal limit or past the key
-// count, so scores are masked and V past the key count is zeroed. first:
-// the wave's first sub-block, which always sets the bases.
+// Scores of q tile u over the sub-block's 32 keys: lane (G, c) gets, for q
+// column c, keys 8G .. 8G+7 (the first four from key tile 0, the last four
+// from key tile 1). EDGE: keys at or past the column's visible count are
+// set to -inf.
+template <int QPW, bool EDGE>
+__device__ __forceinline__ void scores(const u32x4 (&k)[4], const u32x4 (&qop)[QPW][2], int u,
+                                       int kb, int G, const int (&nq)[QPW], float (&sc)[8]) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  f32x4 sa = mfma(k[0], qop[u][0], z);
+  f32x4 sb = mfma(k[2], qop[u][0], z);
+  sa = mfma(k[1], qop[u][1], sa);
+  sb = mfma(k[3], qop[u][1], sb);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sc[i] = sa[i];
+    sc[4 + i] = sb[i];
+  }
+  if constexpr (EDGE) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      if (kb + 8 * G + jj >= nq[u]) sc[jj] = -__builtin_inff();
+  }
+}
+
+// One 32-key sub-block for QPW q tiles. The scores of every q tile come
+// first, with the lane's max score of each; one wave-uniform test then says
+// whether any score exceeds its column's threshold (or this is the wave's
+// first sub-block), in which case every q tile rebases (rare). The weights
+// and accumulation of every q tile follow the join, in place over the
+// scores, so nothing is computed twice and the accumulators stay in their
+// registers on both paths. EDGE: the sub-block reaches past some row's
+// causal limit or past the key count, so scores are masked and V past the
+// key count is zeroed.
 template <int QPW, bool EDGE>
 __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, bool first,
-                                          const u32x4 (&qop)[QPW][2], const char* qlds,
-                                          const int (&nq)[QPW], WaveState<QPW>& st, int lane,
-                                          uint32_t kr0) {
+                                          const u32x4 (&qop)[QPW][2], const int (&nq)[QPW],
+                                          WaveState<QPW>& st, int lane, uint32_t kr0) {
   const int G = lane >> 4;
-  const float ninf = -__builtin_inff();
   auto rd = [&](uint32_t off) { return *reinterpret_cast<const u32x4*>(sub + off); };
   // d-step 1 flips bit 2 of the chunk index; computed here by an opaque
-  // instruction so that it is not hoisted into a second register that the
-  // four-q-tile loop cannot spare
+  // instruction so that it is not hoisted into a second live register
   uint32_t kr1;
   asm volatile("v_xor_b32 %0, 64, %1" : "=v"(kr1) : "v"(kr0));
-  const u32x4 ka0 = rd(kr0);
-  const u32x4 ka1 = rd(kr1);
-  const u32x4 kb0 = rd(kr0 + 512);
-  const u32x4 kb1 = rd(kr1 + 512);
+  const u32x4 k[4] = {rd(kr0), rd(kr1), rd(kr0 + 512), rd(kr1 + 512)};
+  float sc[QPW][8];
+  float smax[QPW];
+  bool over = false;
+#pragma unroll
+  for (int u = 0; u < QPW; ++u) {
+    scores<QPW, EDGE>(k, qop, u, kb, G, nq, sc[u]);
+    smax[u] = max3(max3(sc[u][0], sc[u][1], sc[u][2]), max3(sc[u][3], sc[u][4], sc[u][5]),
+                   __builtin_elementwise_maximum(sc[u][6], sc[u][7]));
+    st.ms[u] = __builtin_elementwise_maximum(st.ms[u], smax[u]);
+    over |= smax[u] > st.thr[u];
+  }
+  if (first || __any(over)) {
+#pragma unroll
+    for (int u = 0; u < QPW; ++u) rebase<QPW>(st, u, smax[u]);
+  }
+  // V operands only now: K is dead, so the two are never live together
   u32x4 v[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) v[dt] = rd(4096 + dt * 1024 + lane * 16);
@@ -259,38 +273,7 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, boo
     }
   }
 #pragma unroll
-  for (int u = 0; u < QPW; ++u) {
-    u32x4 q0, q1;
-    if constexpr (q_in_lds<QPW>()) {
-      q0 = *reinterpret_cast<const u32x4*>(qlds + (2 * u) * 1024 + lane * 16);
-      q1 = *reinterpret_cast<const u32x4*>(qlds + (2 * u + 1) * 1024 + lane * 16);
-    } else {
-      q0 = qop[u][0];
-      q1 = qop[u][1];
-    }
-    f32x4 sa = mfma(ka0, q0, f32x4{0.f, 0.f, 0.f, 0.f});
-    sa = mfma(ka1, q1, sa);
-    f32x4 sb = mfma(kb0, q0, f32x4{0.f, 0.f, 0.f, 0.f});
-    sb = mfma(kb1, q1, sb);
-    float sc[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-    if constexpr (EDGE) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        if (kb + 8 * G + jj >= nq[u]) sc[jj] = ninf;
-    }
-    // Each path finishes the q tile itself (weights into l, pm and the PV
-    // MFMAs): were the paths to join before the accumulation, the join
-    // would cost register copies of the weights and the state on the
-    // common path.
-    if (first || __any(weights_over(sc, st.nmc[u]))) {
-      rebase<QPW>(st, u, sc);
-      accumulate<QPW>(st, u, sc, v);
-    } else {
-      accumulate<QPW>(st, u, sc, v);
-    }
-    // keep one q tile's temporaries live at a time (four tiles would spill)
-    if constexpr (QPW >= 4) __builtin_amdgcn_sched_barrier(0);
-  }
+  for (int u = 0; u < QPW; ++u) accumulate<QPW>(st, u, sc[u], v);
 }
 
 // One q tile's state as the waves fold it at the end: o accumulators, the
@@ -321,8 +304,10 @@ __device__ __forceinline__ void fold(TileState& a, const TileState& b) {
 }
 
 template <int QPW>
-__device__ __forceinline__ TileState tile_of(const WaveState<QPW>& st, int u) {
-  return TileState{{st.acc[0][u], st.acc[1][u], st.acc[2][u], st.acc[3][u]}, st.mref[u], st.mtrue[u], st.l[u]};
+__device__ __forceinline__ TileState tile_of(const WaveState<QPW>& st, const float (&mtrue)[QPW],
+                                             int u) {
+  return TileState{{st.acc[0][u], st.acc[1][u], st.acc[2][u], st.acc[3][u]}, st.mref[u], mtrue[u],
+                   st.l[u]};
 }
 
 // A published tile state in LDS: per lane 4 f32x4 of o, then mref, mtrue, l
@@ -354,8 +339,7 @@ template <int QPW, int AUX>
 __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
                                           const uint16_t* __restrict__ Q, float* __restrict__ po,
                                           float* __restrict__ pml, const asv_work wk,
-                                          char* __restrict__ ringA, char* __restrict__ ringB,
-                                          char* __restrict__ qlds) {
+                                          char* __restrict__ ringA, char* __restrict__ ringB) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = lane >> 4;
@@ -382,49 +366,32 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
   const uint32_t voff = uint32_t(c16 * 64 + G * 16);  // V^T[16dt + c16][8G .. 8G+7]
   const uint32_t kr0 = k_read(G, c16, 0);
 
-  // Q operands (B of the score MFMA) and each column's visible key count.
-  // Wide tiles: wave w fetches q tile w into the block's Q area in operand
-  // order (tile u, d-step s at (2u + s)*1 KB + lane*16); the barrier after
-  // the ring's first fill publishes it.
+  // Q operands (B of the score MFMA, held in registers for the whole item)
+  // and each column's visible key count
   WaveState<QPW> st;
   u32x4 qop[QPW][2];
   int nq[QPW];
   const float ninf = -__builtin_inff();
-  auto q_ptr = [&](int u) -> const uint16_t* {
-    const int q = u * 16 + c16;
-    return Q + (int64_t(T.row0 + (q >> 2)) * ASV_Q_HEADS + g * 4 + (q & 3)) * ASV_HEAD_DIM + 8 * G;
-  };
-  if constexpr (q_in_lds<QPW>()) {
-    const int u = wave;
-    u32x4 a = u32x4{0u, 0u, 0u, 0u}, b = u32x4{0u, 0u, 0u, 0u};
-    if (((u * 16 + c16) >> 2) < T.nrows) {
-      a = load16(q_ptr(u));
-      b = load16(q_ptr(u) + 32);
-    }
-    *reinterpret_cast<u32x4*>(qlds + (2 * u) * 1024 + lane * 16) = a;
-    *reinterpret_cast<u32x4*>(qlds + (2 * u + 1) * 1024 + lane * 16) = b;
-  }
 #pragma unroll
   for (int u = 0; u < QPW; ++u) {
     const int q = u * 16 + c16;
     const int rt = q >> 2;
     if (rt < T.nrows) {
-      if constexpr (!q_in_lds<QPW>()) {
-        qop[u][0] = load16(q_ptr(u));
-        qop[u][1] = load16(q_ptr(u) + 32);
-      }
+      const uint16_t* qp =
+          Q + (int64_t(T.row0 + rt) * ASV_Q_HEADS + g * 4 + (q & 3)) * ASV_HEAD_DIM + 8 * G;
+      qop[u][0] = load16(qp);
+      qop[u][1] = load16(qp + 32);
       nq[u] = gload(tv.rows + T.row0 + rt).nkeys;
     } else {
-      if constexpr (!q_in_lds<QPW>()) {
-        qop[u][0] = u32x4{0u, 0u, 0u, 0u};
-        qop[u][1] = u32x4{0u, 0u, 0u, 0u};
-      }
+      qop[u][0] = u32x4{0u, 0u, 0u, 0u};
+      qop[u][1] = u32x4{0u, 0u, 0u, 0u};
       nq[u] = 0;
     }
     st.mref[u] = ninf;
     st.nmc[u] = 0.f;
+    st.thr[u] = ninf;
+    st.ms[u] = ninf;
     st.l[u] = 0.f;
-    st.pm[u] = 0u;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) st.acc[dt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -443,48 +410,43 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
   } else {
     wait_vm<0>();
   }
-  if constexpr (q_in_lds<QPW>()) __syncthreads();  // the Q area is written
 
-  // two-slot ring: while one slot is consumed the next sub-block's 8 loads
-  // are in flight
-  for (int i = 0; i < nb; i += 2) {
+  // two-slot ring, one sub-block an iteration: while one slot is consumed
+  // the next sub-block's 8 loads are in flight into the other. The wave's
+  // sub-blocks that reach past the tile's first row's causal limit (edge
+  // sub-blocks, masked) all come after the interior ones, so the two kinds
+  // run in two loops, each with one copy of the sub-block code: values then
+  // stay in their registers from one iteration to the next.
+  auto step = [&](int i) -> const char* {
+    const bool odd = (i & 1) != 0;
     if (i + 1 < nb) {
-      issue_sub<AUX>(slotB, Kh, Vh, first + (i + 1) * stride, koff, voff);
+      issue_sub<AUX>(odd ? slotA : slotB, Kh, Vh, first + (i + 1) * stride, koff, voff);
       wait_vm<8>();
     } else {
       wait_vm<0>();
     }
-    {
-      const int kb = first + i * stride;
-      if (kb + 32 > n_first)
-        sub_block<QPW, true>(slotA, kb, S.keys, i == 0, qop, qlds, nq, st, lane, kr0);
-      else
-        sub_block<QPW, false>(slotA, kb, S.keys, i == 0, qop, qlds, nq, st, lane, kr0);
-    }
-    if (i + 1 >= nb) break;
-    if (i + 2 < nb) {
-      issue_sub<AUX>(slotA, Kh, Vh, first + (i + 2) * stride, koff, voff);
-      wait_vm<8>();
-    } else {
-      wait_vm<0>();
-    }
-    {
-      const int kb = first + (i + 1) * stride;
-      if (kb + 32 > n_first)
-        sub_block<QPW, true>(slotB, kb, S.keys, false, qop, qlds, nq, st, lane, kr0);
-      else
-        sub_block<QPW, false>(slotB, kb, S.keys, false, qop, qlds, nq, st, lane, kr0);
-    }
+    return odd ? slotB : slotA;
+  };
+  // interior: first + i * stride + 32 <= n_first
+  const int lim = n_first - 32 - first;
+  const int n_in = lim < 0 ? 0 : min(nb, lim / stride + 1);
+  int i = 0;
+  for (; i < n_in; ++i) {
+    const char* cur = step(i);
+    sub_block<QPW, false>(cur, first + i * stride, S.keys, i == 0, qop, nq, st, lane, kr0);
+  }
+  for (; i < nb; ++i) {
+    const char* cur = step(i);
+    sub_block<QPW, true>(cur, first + i * stride, S.keys, i == 0, qop, nq, st, lane, kr0);
   }
   // column sums and true maxima (the four lanes of a column hold its keys
   // 8G..8G+7 of every sub-block; their bases are equal)
   const float c = kScale * kLog2e;
+  float mtrue[QPW];
 #pragma unroll
   for (int u = 0; u < QPW; ++u) {
     st.l[u] = add_xor32(add_xor16(st.l[u]));
-    const uint32_t pc = umax_xor32(umax_xor16(st.pm[u]));
-    st.pm[u] = pc;
-    st.mtrue[u] = (pc == 0u) ? ninf : st.mref[u] + __builtin_amdgcn_logf(__uint_as_float(pc)) / c;
+    mtrue[u] = max_xor32(max_xor16(st.ms[u]));
   }
   __syncthreads();  // the rings are reused for the fold
 
@@ -501,14 +463,14 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
   static_assert(6 * kTileFloats * 4 <= kWaves * kSubBytes, "published states fit the ring");
 #pragma unroll
   for (int u = 0; u < QPW; ++u)
-    if (u != wave) put_tile(slot(wave, u), tile_of(st, u), lane);
+    if (u != wave) put_tile(slot(wave, u), tile_of(st, mtrue, u), lane);
   __syncthreads();
   if (wave >= QPW) return;
   const int u = wave;
   TileState own;
 #pragma unroll
   for (int t = 0; t < QPW; ++t)
-    if (t == u) own = tile_of(st, t);
+    if (t == u) own = tile_of(st, mtrue, t);
   TileState a = (u == 0) ? own : get_tile(slot(0, u), lane);
   for (int w = 1; w < kWaves; ++w) fold(a, (w == u) ? own : get_tile(slot(w, u), lane));
 
@@ -543,7 +505,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split(TableView tv, int laye
   // being loaded from the one being read; the fold reuses them afterwards
   __shared__ __attribute__((aligned(16))) char ringA[kWaves * kSubBytes];
   __shared__ __attribute__((aligned(16))) char ringB[kWaves * kSubBytes];
-  __shared__ __attribute__((aligned(16))) char qarea[QPW_MAX >= 4 ? 8 * 1024 : 16];
   const asv_work wk = uniform(cload(tv.work + blockIdx.x));
   const asv_tile T = uniform(cload(tv.tiles + wk.tile));
   const int nqt = (T.nrows + 3) >> 2;
@@ -552,24 +513,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split(TableView tv, int laye
   const bool once = uni(cload(tv.segs + T.stream).rows) <= ASV_TILE_ROWS;
   if constexpr (QPW_MAX >= 4) {
     if (nqt == 4) {
-      if (once) return attn_item<4, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
-      return attn_item<4, 0>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
+      if (once) return attn_item<4, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB);
+      return attn_item<4, 0>(tv, layer, Q, po, pml, wk, ringA, ringB);
     }
   }
   if constexpr (QPW_MAX >= 3) {
     if (nqt == 3) {
-      if (once) return attn_item<3, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
-      return attn_item<3, 0>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
+      if (once) return attn_item<3, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB);
+      return attn_item<3, 0>(tv, layer, Q, po, pml, wk, ringA, ringB);
     }
   }
   if constexpr (QPW_MAX >= 2) {
     if (nqt == 2) {
-      if (once) return attn_item<2, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
-      return attn_item<2, 0>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
+      if (once) return attn_item<2, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB);
+      return attn_item<2, 0>(tv, layer, Q, po, pml, wk, ringA, ringB);
     }
   }
-  if (once) return attn_item<1, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
-  attn_item<1, 0>(tv, layer, Q, po, pml, wk, ringA, ringB, qarea);
+  if (once) return attn_item<1, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB);
+  attn_item<1, 0>(tv, layer, Q, po, pml, wk, ringA, ringB);
 }
 
 }  // namespace
