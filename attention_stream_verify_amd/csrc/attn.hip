@@ -13,7 +13,10 @@
 // tiles (their Q operands in registers) and streams its own quarter of the
 // split's keys (32-key sub-blocks w, w+4, ...) through a private LDS ring
 // that direct global->LDS loads fill; at the end the four waves fold their
-// states through LDS in wave order.
+// states through LDS in wave order. Streams of more than one tile (prompt
+// chunks) are split into group items instead: up to four consecutive tiles,
+// one a wave, that walk the split's keys together through one shared ring
+// (attn_group below).
 //
 // Per 32-key sub-block, on the bf16 16x16x32 MFMA (fp32 accumulate):
 //   S^T[key][q]  = K[key][:] . Q[q][:]        (2 key tiles x 2 d-steps)
@@ -28,10 +31,10 @@
 // as two bf16 parts (hi = the top 16 bits of the fp32 weight, lo = the
 // rest) so the partials keep ~16 bits of the weights, not bf16's 8.
 //
-// Bits depend only on the item's own stream: the split plan comes from the
-// stream's rows and keys, each item writes its own records, and the fold
-// order is fixed, so a shared round gives the same bits as each stream run
-// alone.
+// Bits depend only on the item's own stream: the split plan and the grouping
+// of its tiles come from the stream's rows and keys, each item writes its
+// own records, and the fold order is fixed, so a shared round gives the same
+// bits as each stream run alone.
 
 #include "device.h"
 
@@ -225,6 +228,41 @@ __device__ __forceinline__ void scores(const u32x4 (&k)[4], const u32x4 (&qop)[Q
   }
 }
 
+// LDS reads the compiler does not see, for the shared ring of group items:
+// its slot is chosen at run time, so the compiler cannot tell the slot being
+// read from the ones the direct loads are filling, and before a plain read
+// it would wait for every load in flight (vmcnt(0)). Each statement waits
+// for its own reads' results (lgkmcnt(0)) before it ends.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return uint32_t(size_t((__attribute__((address_space(3))) const char*)(p)));
+}
+
+// K operands: rows at a0 and a1 (d-steps 0 and 1), key tile 1 512 bytes on
+__device__ __forceinline__ void lds_read_k(u32x4 (&k)[4], uint32_t a0, uint32_t a1) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %4 offset:512\n\t"
+      "ds_read_b128 %3, %5 offset:512\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+
+// V operands of the four d tiles, 1 KB apart from a
+__device__ __forceinline__ void lds_read_v(u32x4 (&v)[4], uint32_t a) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "ds_read_b128 %3, %4 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(a)
+      : "memory");
+}
+
 // One 32-key sub-block for QPW q tiles. The scores of every q tile come
 // first, with the lane's max score of each; one wave-uniform test then says
 // whether any score exceeds its column's threshold (or this is the wave's
@@ -234,7 +272,7 @@ __device__ __forceinline__ void scores(const u32x4 (&k)[4], const u32x4 (&qop)[Q
 // registers on both paths. EDGE: the sub-block reaches past some row's
 // causal limit or past the key count, so scores are masked and V past the
 // key count is zeroed.
-template <int QPW, bool EDGE>
+template <int QPW, bool EDGE, bool OPAQUE = false>
 __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, bool first,
                                           const u32x4 (&qop)[QPW][2], const int (&nq)[QPW],
                                           WaveState<QPW>& st, int lane, uint32_t kr0) {
@@ -244,7 +282,16 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, boo
   // instruction so that it is not hoisted into a second live register
   uint32_t kr1;
   asm volatile("v_xor_b32 %0, 64, %1" : "=v"(kr1) : "v"(kr0));
-  const u32x4 k[4] = {rd(kr0), rd(kr1), rd(kr0 + 512), rd(kr1 + 512)};
+  u32x4 k[4];
+  if constexpr (OPAQUE) {
+    const uint32_t base = lds_addr(sub);
+    lds_read_k(k, base + kr0, base + kr1);
+  } else {
+    k[0] = rd(kr0);
+    k[1] = rd(kr1);
+    k[2] = rd(kr0 + 512);
+    k[3] = rd(kr1 + 512);
+  }
   float sc[QPW][8];
   float smax[QPW];
   bool over = false;
@@ -262,8 +309,12 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, boo
   }
   // V operands only now: K is dead, so the two are never live together
   u32x4 v[4];
+  if constexpr (OPAQUE) {
+    lds_read_v(v, lds_addr(sub) + 4096 + lane * 16);
+  } else {
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) v[dt] = rd(4096 + dt * 1024 + lane * 16);
+    for (int dt = 0; dt < 4; ++dt) v[dt] = rd(4096 + dt * 1024 + lane * 16);
+  }
   if constexpr (EDGE) {
     if (kb + 32 > keys) {  // slots past the key count may hold anything
 #pragma unroll
@@ -496,6 +547,165 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
   }
 }
 
+// Group items (ntiles > 1): up to four consecutive 16-row tiles of one
+// multi-tile stream (a prompt chunk) and one split. Wave w owns tile w of
+// the group, all four of its q tiles, and walks every sub-block of the
+// split; the four waves share one ring of kGroupSlots sub-blocks, each wave
+// filling a quarter of every sub-block (K group w and V group w, 2 KB), with
+// one block barrier a sub-block. Each K/V byte so enters LDS once for up to
+// four tiles where single-tile items fetch it once a tile, which cuts the
+// L2 requests of chunks fourfold, and there is no fold between waves.
+constexpr int kGroupSlots = 8;  // 64 KB: both ring arrays
+
+// Block barrier of the shared ring. __syncthreads() would also wait for
+// every LDS write the wave has in flight, the ring's direct loads included
+// (vmcnt(0)), which would drain the ring at every sub-block; the loads that
+// must have landed are waited for explicitly before this. The empty asm
+// statements keep the compiler from moving memory accesses across it, and
+// lgkmcnt(0) retires the wave's LDS reads of the slot about to be refilled.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt: no wait
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int AUX>
+__device__ __forceinline__ void issue_quarter(char* slot, const uint16_t* __restrict__ Kh,
+                                              const uint16_t* __restrict__ Vh, int kb,
+                                              uint32_t koff, uint32_t voff, int wave) {
+  const char* kbase = reinterpret_cast<const char*>(Kh + int64_t(kb) * ASV_HEAD_DIM);
+  const char* vbase =
+      reinterpret_cast<const char*>(Vh + int64_t(kb >> 5) * (ASV_HEAD_DIM * 32)) + wave * 1024;
+  lds_dma16<AUX>(kbase, koff, slot + wave * 1024);
+  lds_dma16<AUX>(vbase, voff, slot + 4096 + wave * 1024);
+}
+
+template <int AUX>
+__device__ __forceinline__ void attn_group(const TableView& tv, int layer,
+                                           const uint16_t* __restrict__ Q, float* __restrict__ po,
+                                           float* __restrict__ pml, const asv_work wk,
+                                           char* __restrict__ ringA, char* __restrict__ ringB) {
+  constexpr int QPW = 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = lane >> 4;
+  const int c16 = lane & 15;
+  const bool active = wave < wk.ntiles;
+  const asv_tile T0 = uniform(cload(tv.tiles + wk.tile));
+  const asv_tile TL = uniform(cload(tv.tiles + wk.tile + wk.ntiles - 1));
+  const asv_tile T = uniform(cload(tv.tiles + wk.tile + (active ? wave : 0)));
+  const asv_seg S = uniform(cload(tv.segs + T0.stream));
+  const int g = wk.head;
+  // the group's first row sees the fewest keys, its last row the most
+  const int n_first = uni(cload(tv.rows + T0.row0).nkeys);
+  const int n_last = uni(cload(tv.rows + TL.row0 + TL.nrows - 1).nkeys);
+  const int k0 = split_start(S, wk.split);
+  const int k1 = min(split_start(S, wk.split + 1), n_last);
+  const int64_t head_elems = int64_t(S.cap) * ASV_HEAD_DIM;
+  const int64_t sel = int64_t(layer) * tv.n_streams + T0.stream;
+  const uint16_t* Kh = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.kp + sel))) + g * head_elems;
+  const uint16_t* Vh = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.vp + sel))) + g * head_elems;
+
+  // this wave's quarter of each sub-block: K group `wave`, V group `wave`
+  const uint32_t koff = uint32_t(wave * 1024) + k_fetch(lane, wave);
+  const uint32_t voff = uint32_t(c16 * 64 + G * 16);
+  const uint32_t kr0 = k_read(G, c16, 0);
+
+  WaveState<QPW> st;
+  u32x4 qop[QPW][2];
+  int nq[QPW];
+  const float ninf = -__builtin_inff();
+#pragma unroll
+  for (int u = 0; u < QPW; ++u) {
+    const int q = u * 16 + c16;
+    const int rt = q >> 2;
+    if (active && rt < T.nrows) {
+      const uint16_t* qp =
+          Q + (int64_t(T.row0 + rt) * ASV_Q_HEADS + g * 4 + (q & 3)) * ASV_HEAD_DIM + 8 * G;
+      qop[u][0] = load16(qp);
+      qop[u][1] = load16(qp + 32);
+      nq[u] = gload(tv.rows + T.row0 + rt).nkeys;
+    } else {
+      qop[u][0] = u32x4{0u, 0u, 0u, 0u};
+      qop[u][1] = u32x4{0u, 0u, 0u, 0u};
+      nq[u] = 0;
+    }
+    st.mref[u] = ninf;
+    st.nmc[u] = 0.f;
+    st.thr[u] = ninf;
+    st.ms[u] = ninf;
+    st.l[u] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.acc[dt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto slot = [&](int s) -> char* {
+    return ((s & 4) ? ringB : ringA) + (s & 3) * kSubBytes;
+  };
+  const int nb = (k1 - k0 + 31) >> 5;  // >= 1: an item exists only for visible keys
+  // prologue: the first kGroupSlots - 1 sub-blocks in flight. Always as
+  // many loads (a split of fewer sub-blocks re-reads its last one into the
+  // spare slots), so that the wait below retires the Q loads on every path
+  // and the compiler adds no wait of its own for them inside the loop.
+#pragma unroll
+  for (int s = 0; s < kGroupSlots - 1; ++s)
+    issue_quarter<AUX>(slot(s), Kh, Vh, k0 + 32 * min(s, nb - 1), koff, voff, wave);
+  wait_vm<2 * (kGroupSlots - 2)>();
+
+  // Iteration i: this wave's loads of sub-block i have landed (older loads
+  // retire first), then the barrier says every wave's have, and that every
+  // wave is done with sub-block i - 1, whose slot is refilled with sub-block
+  // i + kGroupSlots - 1 before sub-block i is computed.
+  auto step = [&](int i) -> const char* {
+    if (i + kGroupSlots - 2 < nb) wait_vm<2 * (kGroupSlots - 2)>();
+    else wait_vm<0>();
+    ring_barrier();
+    const int nx = i + kGroupSlots - 1;
+    if (nx < nb) issue_quarter<AUX>(slot(nx & (kGroupSlots - 1)), Kh, Vh, k0 + 32 * nx, koff, voff, wave);
+    return slot(i & (kGroupSlots - 1));
+  };
+  // interior sub-blocks: every row of the group sees all of their keys
+  const int lim = n_first - 32 - k0;
+  const int n_in = lim < 0 ? 0 : min(nb, lim / 32 + 1);
+  int i = 0;
+  for (; i < n_in; ++i) {
+    const char* cur = step(i);
+    if (active) sub_block<QPW, false, true>(cur, k0 + 32 * i, S.keys, i == 0, qop, nq, st, lane, kr0);
+  }
+  for (; i < nb; ++i) {
+    const char* cur = step(i);
+    if (active) sub_block<QPW, true, true>(cur, k0 + 32 * i, S.keys, i == 0, qop, nq, st, lane, kr0);
+  }
+  if (!active) return;
+
+  // records of the wave's own tile: o = acc / l, then (true max in score
+  // units, l taken to the true max)
+  const float c = kScale * kLog2e;
+#pragma unroll
+  for (int u = 0; u < QPW; ++u) {
+    const float L = add_xor32(add_xor16(st.l[u]));
+    const float mt = max_xor32(max_xor16(st.ms[u]));
+    const int q = u * 16 + c16;
+    const int rt = q >> 2;
+    if (rt < T.nrows) {
+      const int64_t rec =
+          S.poff + (int64_t(wk.split) * S.rows + T.pos0 + rt) * ASV_Q_HEADS + g * 4 + (q & 3);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        f32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = (L > 0.f) ? st.acc[dt][u][e] / L : 0.f;
+        store16f(po + rec * ASV_HEAD_DIM + dt * 16 + 4 * G, r);
+      }
+      if (G == 0) {
+        const float lt = (mt == ninf) ? 0.f : L * exp2_((st.mref[u] - mt) * c);
+        gstore(reinterpret_cast<float2*>(pml) + rec, make_float2((mt == ninf) ? ninf : mt * kScale, lt));
+      }
+    }
+  }
+}
+
 template <int QPW_MAX>
 __global__ __launch_bounds__(kThreads, 2) void attn_split(TableView tv, int layer,
                                                           const uint16_t* __restrict__ Q,
@@ -508,10 +718,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split(TableView tv, int laye
   const asv_work wk = uniform(cload(tv.work + blockIdx.x));
   const asv_tile T = uniform(cload(tv.tiles + wk.tile));
   const int nqt = (T.nrows + 3) >> 2;
-  // a stream of one tile reads its K/V in exactly one item: stream it past
-  // the caches; tiles of a longer stream re-read the same keys
-  const bool once = uni(cload(tv.segs + T.stream).rows) <= ASV_TILE_ROWS;
+  // an item that covers every tile of its stream reads its K/V once: stream
+  // it past the caches; items of a longer stream re-read the same keys
+  const bool once =
+      T.pos0 == 0 && uni(cload(tv.segs + T.stream).rows) <= ASV_TILE_ROWS * int(wk.ntiles);
   if constexpr (QPW_MAX >= 4) {
+    // groups come only from streams of more than one tile, whose tiles
+    // (the last aside) hold 16 rows, so a round that has them launches this
+    // instance
+    if (wk.ntiles > 1) {
+      if (once) return attn_group<kStream>(tv, layer, Q, po, pml, wk, ringA, ringB);
+      return attn_group<0>(tv, layer, Q, po, pml, wk, ringA, ringB);
+    }
     if (nqt == 4) {
       if (once) return attn_item<4, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB);
       return attn_item<4, 0>(tv, layer, Q, po, pml, wk, ringA, ringB);

@@ -70,6 +70,10 @@ int32_t split_start(const Plan& p, int32_t t) {
 }
 
 static_assert(sizeof(asv_seg) == 48, "asv_seg layout");
+static_assert(sizeof(asv_work) == 16, "asv_work layout");
+
+// Tiles of one group item (one a wave of the attention block).
+constexpr int32_t kGroupTiles = 4;
 
 int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
 
@@ -193,22 +197,32 @@ int build_table(const asv_stream_desc* streams, int32_t n_streams, const void* c
     row0 += d.rows;
   }
 
-  // ---- attention work: (tile, kv head, split) for every split holding a key
-  // the tile's last row sees; most keys first so long items start early.
+  // ---- attention work: (tiles, kv head, split) for every split holding a
+  // key the last row of the item's last tile sees. A stream of one tile is
+  // one item a split and head; a longer stream (a prompt chunk) is cut into
+  // groups of up to kGroupTiles consecutive tiles, which read each key once
+  // for the whole group. Costliest first, so long items start early.
   std::vector<asv_work> work;
-  for (int32_t ti = 0; ti < static_cast<int32_t>(tiles.size()); ++ti) {
+  for (int32_t ti = 0; ti < static_cast<int32_t>(tiles.size());) {
     const asv_tile& t = tiles[ti];
     const asv_seg& g = segs[t.stream];
-    const int32_t n_last = full ? g.keys : g.keys - g.rows + t.pos0 + t.nrows;
+    const int32_t stream_tiles = (g.rows + ASV_TILE_ROWS - 1) / ASV_TILE_ROWS;
+    const int32_t left = stream_tiles - t.pos0 / ASV_TILE_ROWS;
+    const int32_t nt = stream_tiles == 1 ? 1 : std::min(kGroupTiles, left);
+    const asv_tile& tl = tiles[ti + nt - 1];
+    const int32_t n_last = full ? g.keys : g.keys - g.rows + tl.pos0 + tl.nrows;
     const Plan pl{g.split_keys, g.split_tail, g.nbig, g.nsplit};
     for (int32_t sp = 0; sp < g.nsplit && split_start(pl, sp) < n_last; ++sp) {
       const int32_t k0 = split_start(pl, sp);
       const int32_t k1 = std::min(sp + 1 < g.nsplit ? split_start(pl, sp + 1) : g.keys, n_last);
-      for (int32_t h = 0; h < ASV_KV_HEADS; ++h) work.push_back({ti, h, sp, k1 - k0});
+      for (int32_t h = 0; h < ASV_KV_HEADS; ++h)
+        work.push_back({ti, int16_t(h), int16_t(nt), sp, k1 - k0});
     }
+    ti += nt;
   }
+  auto cost = [](const asv_work& w) { return int64_t(w.keys) * (w.ntiles > 1 ? 4 : 1); };
   std::stable_sort(work.begin(), work.end(),
-                   [](const asv_work& a, const asv_work& b) { return a.keys > b.keys; });
+                   [&](const asv_work& a, const asv_work& b) { return cost(a) > cost(b); });
 
   // ---- blob layout
   asv_table_info in;

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define ASV_ABI_VERSION 2
+#define ASV_ABI_VERSION 3
 
 /* Model dimensions compiled into the kernels (LFM2.5-24B-A2B shapes). */
 #define ASV_HIDDEN 2048          /* conv channels, attention row width      */
@@ -116,12 +116,20 @@ typedef struct {      /* runs of <= 16 rows of one stream                  */
   int32_t pos0;
 } asv_tile;
 
-typedef struct {      /* one attention work item: (tile, kv head, split)  */
-  int32_t tile;
-  int32_t head;
+typedef struct {      /* one attention work item: (tiles, kv head, split) */
+  int32_t tile;       /* its first tile                                   */
+  int16_t head;
+  int16_t ntiles;     /* 1: one tile, its keys striped over the block's
+                         waves; 2-4: that many consecutive tiles of one
+                         stream, a wave each, every wave walking all of
+                         the split's keys (streams of more than one tile
+                         are cut into groups of 4 tiles, the last shorter) */
   int32_t split;
-  int32_t keys;       /* keys the item visits (its cost)                  */
+  int32_t keys;       /* keys the item visits: the split's keys that the
+                         last row of its last tile sees                   */
 } asv_work;
+/* The work list is ordered by cost, largest first: keys for one-tile
+ * items, 4 x keys for groups (each wave walks every key). */
 
 /* What asv_seg_table_build reports (host). Offsets are byte offsets of the
  * arrays inside the blob; the same struct is passed back to every call. */
@@ -139,7 +147,7 @@ typedef struct {
   int64_t off_segs;        /* asv_seg[n_streams]                              */
   int64_t off_rows;        /* asv_row[n_rows]                                 */
   int64_t off_tiles;       /* asv_tile[n_tiles]                               */
-  int64_t off_work;        /* asv_work[n_work], most keys first               */
+  int64_t off_work;        /* asv_work[n_work], costliest first               */
   int64_t off_conv_state;  /* uint64 device addresses [n_conv_layers][n_streams] */
   int64_t off_k;           /* uint64 device addresses [n_attn_layers][n_streams] */
   int64_t off_v;           /* uint64 device addresses [n_attn_layers][n_streams] */

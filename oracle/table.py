@@ -31,8 +31,12 @@ definitions (the readings are listed in the design notes):
 * partial records: stream s owns records [poff_s, poff_s + nsplit_s*w_s*32),
   poff being the exclusive prefix sum of nsplit_s*w_s*32; the record of
   (row r, q head h, split t) is poff_s + (t*w_s + pos_r)*32 + h;
-* work items: for every tile, kv head and split that holds a key the tile's
-  last row can see.
+* work items: a stream of one tile has an item for every kv head and split
+  that holds a key the tile's last row can see; a longer stream (a prompt
+  chunk) is cut into groups of up to 4 consecutive tiles (the last group
+  shorter), each group an item for every kv head and split that holds a key
+  the last row of its last tile can see. An item is (first tile, kv head,
+  split, tiles in it).
 
 Block mode (PR #1391 "lfm2: draft with LiquidAI's DSpark drafter
 (--drafter)", its list of new kernels: the target's attention and merge with
@@ -47,6 +51,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 TILE_ROWS = 16
+GROUP_TILES = 4
 N_Q_HEADS = 32
 N_KV_HEADS = 8
 KEY_BLOCK = 32
@@ -111,7 +116,7 @@ class Table:
     bounds: list                # per stream: split starts, then K_s
     poff: np.ndarray            # S (int64)
     partial_count: int
-    work: np.ndarray            # [n_work, 3]: tile, kv head, split
+    work: np.ndarray            # [n_work, 4]: first tile, kv head, split, tiles
     n_rows: int = field(default=0)
 
     def record(self, r, h, t):
@@ -197,12 +202,17 @@ def build(streams, full=False):
     partial_count = acc
 
     work = []
-    for ti, (s, _r0, n, p0) in enumerate(tiles):
-        n_last = keys[s] if full else keys[s] - rows[s] + p0 + n
-        for t in range(int(np.count_nonzero(bounds[s][:-1] < n_last))):
-            for g in range(N_KV_HEADS):
-                work.append((ti, g, t))
-    work = np.array(work, dtype=np.int64).reshape(-1, 3)
+    for s in range(S):
+        mine = [ti for ti in range(len(tiles)) if tiles[ti][0] == s]
+        groups = [mine] if len(mine) == 1 else \
+            [mine[i:i + GROUP_TILES] for i in range(0, len(mine), GROUP_TILES)]
+        for grp in groups:
+            _s, _r0, n, p0 = tiles[grp[-1]]
+            n_last = keys[s] if full else keys[s] - rows[s] + p0 + n
+            for t in range(int(np.count_nonzero(bounds[s][:-1] < n_last))):
+                for g in range(N_KV_HEADS):
+                    work.append((grp[0], g, t, len(grp)))
+    work = np.array(work, dtype=np.int64).reshape(-1, 4)
 
     return Table(rows=rows, keys=keys, caps=caps, seg_off=seg_off, row_stream=row_stream,
                  row_pos=row_pos, row_nkeys=row_nkeys, tiles=tiles, split=split,

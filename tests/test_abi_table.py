@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(asv._lib.LIB_PATH)
     for name in _declared():
         assert hasattr(L, name), name
-    assert asv.abi_version() == 2
+    assert asv.abi_version() == 3
     assert asv.strerror(-4) == "caller buffer too small"
 
 
@@ -82,13 +82,16 @@ def _compare(streams, full=False):
     for r in range(R):
         tt = o.tiles[rows["tile"][r]]
         assert tt[1] <= r < tt[1] + tt[2]
-    # work items: the same set (their order is a schedule), keys = visited keys
+    # work items: the same set (their order is a schedule), keys = visited
+    # keys, costliest first (a group's waves each walk every key)
     w = t["work"]
-    got = sorted(zip(w["tile"].tolist(), w["head"].tolist(), w["split"].tolist()))
+    got = sorted(zip(w["tile"].tolist(), w["head"].tolist(), w["split"].tolist(),
+                     w["ntiles"].tolist()))
     assert got == sorted(map(tuple, o.work.tolist()))
-    assert all(w["keys"][i] >= w["keys"][i + 1] for i in range(len(w) - 1))
-    for ti, h, sp, k in zip(w["tile"], w["head"], w["split"], w["keys"]):
-        s, _r0, n, p0 = o.tiles[ti]
+    cost = w["keys"].astype(np.int64) * np.where(w["ntiles"] > 1, 4, 1)
+    assert all(cost[i] >= cost[i + 1] for i in range(len(w) - 1))
+    for ti, sp, nt, k in zip(w["tile"], w["split"], w["ntiles"], w["keys"]):
+        s, _r0, n, p0 = o.tiles[ti + nt - 1]
         last = o.keys[s] if full else o.keys[s] - o.rows[s] + p0 + n
         lo, hi = o.split_range(s, sp)
         assert k == min(hi, last) - lo > 0

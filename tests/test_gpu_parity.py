@@ -229,6 +229,15 @@ def test_attention_parity(config):
     _check_layer_by_part(rnd, rb, out, t, _parity_rows(t, config), f"attn {config}")
 
 
+def _edge_rows(t):
+    """Rows of every tile (each wave of every group item), except for the
+    2,048-row, 131,072-key case, where the oracle would take minutes over
+    them: its first and last rows and 24 seeded ones there."""
+    if int(t.keys.sum()) * t.n_rows > 100_000_000:
+        return sample_rows(t, 24, 5)
+    return sample_rows_every_tile(t, 24, 5)
+
+
 @pytest.mark.parametrize("streams", [
     [(1, 1, 32)],                                # one key
     [(16, 16, 32)],                              # window = whole cache
@@ -239,13 +248,16 @@ def test_attention_parity(config):
     [(17, 20000, 20000)],                        # 7,168 x 2 then 5,664; a one-row second tile
     [(16, 14337, 14368), (24, 21505, 21536)],    # 3 and 4 splits, the last one short
     [(2048, 131072, 131072)],                    # both maxima: 2,048 rows, 131,072 keys
+    [(64, 100, 128), (100, 150, 160)],           # groups of 4 and 3 tiles, fewer sub-blocks than ring slots
+    [(96, 9000, 9024)],                          # 6 tiles: a group of 4, then one of 2
+    [(80, 5000, 5024), (1, 40, 64)],             # 5 tiles: a group of 4, then a lone tile
 ])
 def test_attention_edge_shapes(streams):
     rnd = workloads.Round(0, "cuda", n_conv=0, n_attn=1, streams=streams, with_logits=False)
     print(f"\n[parity] attention edge {streams}", flush=True)
     rb, out = run_round(rnd, with_argmax=False)
     t = otable.build(streams)
-    rows = list(range(t.n_rows)) if t.n_rows <= 64 else sample_rows(t, 24, 5)
+    rows = list(range(t.n_rows)) if t.n_rows <= 64 else _edge_rows(t)
     check_attention_layer(rnd, rb, out["partials"][0], out["o"][0], 0, rows, f"edge {streams}")
 
 
@@ -353,13 +365,15 @@ def test_block_attention_parity(config):
     [(16, 7169, 7200)],                          # two split sizes: 4,000 then 3,169 keys
     [(17, 20000, 20000)],                        # 7,168 x 2 then 5,664; a one-row second tile
     [(16, 14337, 14368), (24, 21505, 21536)],    # 3 and 4 splits, the last one short
+    [(64, 100, 128), (100, 150, 160)],           # groups of 4 and 3 tiles, fewer sub-blocks than ring slots
+    [(96, 9000, 9024)],                          # 6 tiles: a group of 4, then one of 2
 ])
 def test_block_attention_edge_shapes(streams):
     rnd = workloads.Round(0, "cuda", n_conv=0, n_attn=1, streams=streams, with_logits=False)
     print(f"\n[parity] block attention edge {streams}", flush=True)
     rb, out = run_round(rnd, with_argmax=False, full=True)
     t = otable.build(streams, full=True)
-    rows = list(range(t.n_rows)) if t.n_rows <= 64 else sample_rows(t, 24, 5)
+    rows = list(range(t.n_rows)) if t.n_rows <= 64 else _edge_rows(t)
     check_attention_layer(rnd, rb, out["partials"][0], out["o"][0], 0, rows,
                           f"block edge {streams}", full=True)
 

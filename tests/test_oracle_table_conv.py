@@ -82,16 +82,33 @@ def _check_invariants(streams, t):
         mine = [t.record(r, h, sp) for r in range(t.seg_off[s], t.seg_off[s + 1])
                 for h in range(32) for sp in range(t.nsplit[s])]
         assert min(mine) == lo and max(mine) == hi - 1
-    # work: exactly the (tile, kv head, split) with a key the tile's last row sees
+    # work: a one-tile stream's tile, a longer stream's groups of 4 tiles,
+    # each with every (kv head, split) holding a key its last row sees
     want = set()
-    for ti, (s, _r0, n, p0) in enumerate(t.tiles):
-        last = streams[s][1] - streams[s][0] + p0 + n
-        for sp in range(t.nsplit[s]):
-            if sp * t.split[s] < last:
-                for g in range(8):
-                    want.add((ti, g, sp))
+    for s in range(S):
+        mine = [ti for ti, tt in enumerate(t.tiles) if tt[0] == s]
+        size = len(mine) if len(mine) == 1 else 4
+        for i in range(0, len(mine), size):
+            grp = mine[i:i + size]
+            _s, _r0, n, p0 = t.tiles[grp[-1]]
+            last = streams[s][1] - streams[s][0] + p0 + n
+            for sp in range(t.nsplit[s]):
+                if t.bounds[s][sp] < last:
+                    for g in range(8):
+                        want.add((grp[0], g, sp, len(grp)))
     got = [tuple(x) for x in t.work.tolist()]
     assert len(got) == len(set(got)) and set(got) == want
+    # every tile of every stream is in exactly one group, groups of 1 only
+    # for one-tile streams
+    firsts = {}
+    for ti, _g, _sp, n in got:
+        firsts[ti] = n
+    covered = sorted(ti + k for ti, n in firsts.items() for k in range(n))
+    assert covered == list(range(len(t.tiles)))
+    for ti, n in firsts.items():
+        s = t.tiles[ti][0]
+        assert all(t.tiles[ti + k][0] == s for k in range(n))
+        assert (n == 1) == (sum(1 for tt in t.tiles if tt[0] == s) == 1)
 
 
 _stream = st.integers(1, 40).flatmap(
