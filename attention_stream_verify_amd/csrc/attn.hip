@@ -61,7 +61,8 @@ __device__ __forceinline__ uint32_t zero_past(uint32_t w, int key, int keys) {
 
 // Per-wave online-softmax state for QPW q tiles. Per q column the wave
 // keeps an exponent base mref (raw score units; -inf until the column has
-// seen a key), nmc = -mref*c, the sum l of its weights at that base, the
+// seen a key), nmc = -mref*c, the sum l of its weights at that base (summed
+// by the MFMA, see accumulate: all four entries hold the column's sum), the
 // largest score ms it has seen, and thr = mref + kLazy/c. A sub-block's
 // scores are tested against thr first; only when one of them exceeds it (a
 // weight above 2^kLazy at the current base), or on the wave's first
@@ -72,8 +73,30 @@ __device__ __forceinline__ uint32_t zero_past(uint32_t w, int key, int keys) {
 template <int QPW>
 struct WaveState {
   f32x4 acc[4][QPW];
-  float mref[QPW], nmc[QPW], thr[QPW], ms[QPW], l[QPW];
+  f32x4 l[QPW];
+  float mref[QPW], nmc[QPW], thr[QPW], ms[QPW];
 };
+
+// Loop-invariant operands of accumulate, each held in registers: a ones
+// matrix (bf16 1.0 in every element) and the bf16 pairs (-1, 0), (0, -1).
+// They pass through an empty asm so the compiler cannot turn them into
+// inline constants: as the packed-bf16 operand of v_dot2c_f32_bf16 it
+// would encode (-1, 0) as the 32-bit constant -1.0, which the hardware
+// reads as the pair (0, -1).
+struct Consts {
+  u32x4 ones;
+  uint32_t neg_lo, neg_hi;
+};
+
+__device__ __forceinline__ Consts make_consts() {
+  Consts k;
+  uint32_t one = 0x3F803F80u, a = 0x0000BF80u, b = 0xBF800000u;
+  asm volatile("" : "+v"(one), "+v"(a), "+v"(b));
+  k.ones = u32x4{one, one, one, one};
+  k.neg_lo = a;
+  k.neg_hi = b;
+  return k;
+}
 
 constexpr float kLazy = 8.f;  // weights stay <= 2^8 between rebases
 
@@ -177,24 +200,33 @@ __device__ __forceinline__ void rebase(WaveState<QPW>& st, int u, float smax) {
   for (int dt = 0; dt < 4; ++dt) st.acc[dt][u] *= alpha;
 }
 
-// q tile u's scores (in place: their weights at the current base) into l
-// and, as bf16 hi + lo, through the PV MFMAs into the accumulators.
+// q tile u's scores (in place: their weights at the current base), as bf16
+// hi + lo, through the PV MFMAs into the accumulators, and through two more
+// MFMAs with a ones matrix into l: the sum over the sub-block's 32 keys of
+// every column lands in all four entries, so l costs no VALU adds and no
+// reduction across lanes at the end.
 template <int QPW>
 __device__ __forceinline__ void accumulate(WaveState<QPW>& st, int u, float (&p)[8],
-                                           const u32x4 (&v)[4]) {
+                                           const u32x4 (&v)[4], const Consts& kc) {
   const float c = kScale * kLog2e;
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) p[jj] = exp2_(__builtin_fmaf(p[jj], c, st.nmc[u]));
-  st.l[u] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   u32x4 hi, lo;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    // hi = top halves of two weights in one v_perm_b32; lo = what they drop
-    const uint32_t a = __float_as_uint(p[2 * w]);
-    const uint32_t b = __float_as_uint(p[2 * w + 1]);
-    hi[w] = __builtin_amdgcn_perm(b, a, 0x07060302u);
-    const float ra = p[2 * w] - __uint_as_float(a & 0xFFFF0000u);
-    const float rb = p[2 * w + 1] - __uint_as_float(b & 0xFFFF0000u);
+    // hi = top halves of two weights in one v_perm_b32; what they drop is
+    // p - hi, exact in fp32, one v_dot2c_f32_bf16 each (hi . (-1, 0) + p)
+    // (the pair is bit-cast from a plain local: a bit cast of the vector
+    // element hi[w] inside this unrolled loop was compiled as hi[0] for
+    // every w)
+    const uint32_t h =
+        __builtin_amdgcn_perm(__float_as_uint(p[2 * w + 1]), __float_as_uint(p[2 * w]), 0x07060302u);
+    hi[w] = h;
+    const bf16x2 hb = __builtin_bit_cast(bf16x2, h);
+    const float ra =
+        __builtin_amdgcn_fdot2_f32_bf16(hb, __builtin_bit_cast(bf16x2, kc.neg_lo), p[2 * w], false);
+    const float rb = __builtin_amdgcn_fdot2_f32_bf16(hb, __builtin_bit_cast(bf16x2, kc.neg_hi),
+                                                     p[2 * w + 1], false);
     lo[w] = __builtin_amdgcn_perm(__float_as_uint(rb), __float_as_uint(ra), 0x07060302u);
   }
 #pragma unroll
@@ -202,6 +234,8 @@ __device__ __forceinline__ void accumulate(WaveState<QPW>& st, int u, float (&p)
     st.acc[dt][u] = mfma(v[dt], hi, st.acc[dt][u]);
     st.acc[dt][u] = mfma(v[dt], lo, st.acc[dt][u]);
   }
+  st.l[u] = mfma(kc.ones, hi, st.l[u]);
+  st.l[u] = mfma(kc.ones, lo, st.l[u]);
 }
 
 // Scores of q tile u over the sub-block's 32 keys: lane (G, c) gets, for q
@@ -275,7 +309,8 @@ __device__ __forceinline__ void lds_read_v(u32x4 (&v)[4], uint32_t a) {
 template <int QPW, bool EDGE, bool OPAQUE = false>
 __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, bool first,
                                           const u32x4 (&qop)[QPW][2], const int (&nq)[QPW],
-                                          WaveState<QPW>& st, int lane, uint32_t kr0) {
+                                          WaveState<QPW>& st, int lane, uint32_t kr0,
+                                          const Consts& kc) {
   const int G = lane >> 4;
   auto rd = [&](uint32_t off) { return *reinterpret_cast<const u32x4*>(sub + off); };
   // d-step 1 flips bit 2 of the chunk index; computed here by an opaque
@@ -324,7 +359,19 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, boo
     }
   }
 #pragma unroll
-  for (int u = 0; u < QPW; ++u) accumulate<QPW>(st, u, sc[u], v);
+  for (int u = 0; u < QPW; ++u) accumulate<QPW>(st, u, sc[u], v, kc);
+  // Schedule: q tile 0's weights first, then every MFMA of the PV and l
+  // products followed by VALU work of the later q tiles. Left alone, the
+  // compiler puts all weights before all MFMAs, and the matrix core idles
+  // while the wave computes weights and the other way round.
+  if constexpr (QPW > 1) {
+    __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);  // VALU: q tile 0
+#pragma unroll
+    for (int i = 0; i < 10 * QPW; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+    }
+  }
 }
 
 // One q tile's state as the waves fold it at the end: o accumulators, the
@@ -358,7 +405,7 @@ template <int QPW>
 __device__ __forceinline__ TileState tile_of(const WaveState<QPW>& st, const float (&mtrue)[QPW],
                                              int u) {
   return TileState{{st.acc[0][u], st.acc[1][u], st.acc[2][u], st.acc[3][u]}, st.mref[u], mtrue[u],
-                   st.l[u]};
+                   st.l[u][0]};
 }
 
 // A published tile state in LDS: per lane 4 f32x4 of o, then mref, mtrue, l
@@ -416,6 +463,7 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
   for (int j = 0; j < 4; ++j) koff[j] = uint32_t(j * 1024) + k_fetch(lane, j);
   const uint32_t voff = uint32_t(c16 * 64 + G * 16);  // V^T[16dt + c16][8G .. 8G+7]
   const uint32_t kr0 = k_read(G, c16, 0);
+  const Consts kc = make_consts();
 
   // Q operands (B of the score MFMA, held in registers for the whole item)
   // and each column's visible key count
@@ -442,7 +490,7 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
     st.nmc[u] = 0.f;
     st.thr[u] = ninf;
     st.ms[u] = ninf;
-    st.l[u] = 0.f;
+    st.l[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) st.acc[dt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -484,21 +532,18 @@ __device__ __forceinline__ void attn_item(const TableView& tv, int layer,
   int i = 0;
   for (; i < n_in; ++i) {
     const char* cur = step(i);
-    sub_block<QPW, false>(cur, first + i * stride, S.keys, i == 0, qop, nq, st, lane, kr0);
+    sub_block<QPW, false>(cur, first + i * stride, S.keys, i == 0, qop, nq, st, lane, kr0, kc);
   }
   for (; i < nb; ++i) {
     const char* cur = step(i);
-    sub_block<QPW, true>(cur, first + i * stride, S.keys, i == 0, qop, nq, st, lane, kr0);
+    sub_block<QPW, true>(cur, first + i * stride, S.keys, i == 0, qop, nq, st, lane, kr0, kc);
   }
-  // column sums and true maxima (the four lanes of a column hold its keys
-  // 8G..8G+7 of every sub-block; their bases are equal)
+  // true maxima (the four lanes of a column saw its keys 8G..8G+7 of every
+  // sub-block; the column sums are already whole)
   const float c = kScale * kLog2e;
   float mtrue[QPW];
 #pragma unroll
-  for (int u = 0; u < QPW; ++u) {
-    st.l[u] = add_xor32(add_xor16(st.l[u]));
-    mtrue[u] = max_xor32(max_xor16(st.ms[u]));
-  }
+  for (int u = 0; u < QPW; ++u) mtrue[u] = max_xor32(max_xor16(st.ms[u]));
   __syncthreads();  // the rings are reused for the fold
 
   // Fold: wave u (u < QPW) owns q tile u. Every wave publishes the states of
@@ -611,6 +656,7 @@ __device__ __forceinline__ void attn_group(const TableView& tv, int layer,
   const uint32_t koff = uint32_t(wave * 1024) + k_fetch(lane, wave);
   const uint32_t voff = uint32_t(c16 * 64 + G * 16);
   const uint32_t kr0 = k_read(G, c16, 0);
+  const Consts kc = make_consts();
 
   WaveState<QPW> st;
   u32x4 qop[QPW][2];
@@ -635,7 +681,7 @@ __device__ __forceinline__ void attn_group(const TableView& tv, int layer,
     st.nmc[u] = 0.f;
     st.thr[u] = ninf;
     st.ms[u] = ninf;
-    st.l[u] = 0.f;
+    st.l[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) st.acc[dt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -671,11 +717,13 @@ __device__ __forceinline__ void attn_group(const TableView& tv, int layer,
   int i = 0;
   for (; i < n_in; ++i) {
     const char* cur = step(i);
-    if (active) sub_block<QPW, false, true>(cur, k0 + 32 * i, S.keys, i == 0, qop, nq, st, lane, kr0);
+    if (active)
+      sub_block<QPW, false, true>(cur, k0 + 32 * i, S.keys, i == 0, qop, nq, st, lane, kr0, kc);
   }
   for (; i < nb; ++i) {
     const char* cur = step(i);
-    if (active) sub_block<QPW, true, true>(cur, k0 + 32 * i, S.keys, i == 0, qop, nq, st, lane, kr0);
+    if (active)
+      sub_block<QPW, true, true>(cur, k0 + 32 * i, S.keys, i == 0, qop, nq, st, lane, kr0, kc);
   }
   if (!active) return;
 
@@ -684,7 +732,7 @@ __device__ __forceinline__ void attn_group(const TableView& tv, int layer,
   const float c = kScale * kLog2e;
 #pragma unroll
   for (int u = 0; u < QPW; ++u) {
-    const float L = add_xor32(add_xor16(st.l[u]));
+    const float L = st.l[u][0];
     const float mt = max_xor32(max_xor16(st.ms[u]));
     const int q = u * 16 + c16;
     const int rt = q >> 2;
