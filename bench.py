@@ -84,7 +84,8 @@ WORKLOAD_KEYS = {0: "tiny", 1: "decode_16x1", 2: "verify_16x8", 3: "long_context
                  4: "scratch_2048"}
 
 
-TRAFFIC_PROFILES = {3: "profiles/attn_split_long_context_traffic.md"}
+TRAFFIC_PROFILES = {3: "profiles/attn_split_long_context_traffic.md",
+                    4: "profiles/attn_split_scratch_traffic.md"}
 
 
 def profiled_traffic(config):
@@ -96,7 +97,10 @@ def profiled_traffic(config):
     return None if f is None else int(f["traffic_bytes_per_launch"])
 
 
-SQ_PROFILES = {3: "profiles/attn_split_long_context_sq_counters.md"}
+SQ_PROFILES = {1: "profiles/attn_split_decode_sq_counters.md",
+               2: "profiles/attn_split_verify_sq_counters.md",
+               3: "profiles/attn_split_long_context_sq_counters.md",
+               4: "profiles/attn_split_scratch_sq_counters.md"}
 
 
 def profile_fields(name, keys):
@@ -496,7 +500,7 @@ def main():
         entries = {}
         del rnd, rb
         m_self = workload_entry(m)
-        m_self.update({"mfma_busy": line["mfma_busy"]})
+        m_self.update({"mfma_busy": line["mfma_busy"], "traffic_bytes": line["roofline"]["traffic"]})
         del m
         for c in range(5):
             if c == args.config and not args.block and not args.with_qk:
@@ -506,6 +510,7 @@ def main():
                                block=args.block, with_qk=args.with_qk, eager=args.eager)
             e = workload_entry(mc)
             e["mfma_busy"] = None if args.block else profiled_mfma(c)
+            e["traffic_bytes"] = None if (args.block or args.with_qk) else profiled_traffic(c)
             entries[WORKLOAD_KEYS[c]] = e
             del mc
             torch.cuda.empty_cache()
