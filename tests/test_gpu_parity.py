@@ -288,7 +288,8 @@ def test_shared_round_equals_each_stream_alone(config):
     P = int(rb.info.partial_count)
     po = out["partials"][0][:P * 64].view(P, 64)
     pml = out["partials"][0][P * 64:].view(P, 2)
-    streams = range(len(rnd.streams)) if config != 4 else [0, 1, 2, 47, 48, len(rnd.streams) - 1]
+    # config 4: some windows and every prompt chunk (48-51: 512, 512, 512 and 40 rows)
+    streams = range(len(rnd.streams)) if config != 4 else [0, 1, 2, 47, 48, 49, 50, 51]
     for s in streams:
         one, off = _slice_round(rnd, s)
         rb1, out1 = run_round(one, with_argmax=False)
@@ -386,7 +387,7 @@ def test_block_shared_round_equals_each_stream_alone(config):
     P = int(rb.info.partial_count)
     po = out["partials"][0][:P * 64].view(P, 64)
     pml = out["partials"][0][P * 64:].view(P, 2)
-    streams = range(len(rnd.streams)) if config != 4 else [0, 1, 47, 48, len(rnd.streams) - 1]
+    streams = range(len(rnd.streams)) if config != 4 else [0, 1, 47, 48, 49, 50, 51]
     for s in streams:
         one, off = _slice_round(rnd, s)
         rb1, out1 = run_round(one, with_argmax=False, full=True)
