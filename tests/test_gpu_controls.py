@@ -77,10 +77,16 @@ def test_control_every_stream_reads_stream0_conv_state():
         _conv_check(rnd, rb.y, states, before)               # planted: red
 
 
-def test_control_every_stream_reads_stream0_kv_cache():
-    print("\n[control] K/V cache of stream 0 read by every stream", flush=True)
+# a prompt chunk (40 rows: one group item of three tiles a head and split)
+# and a 17-row stream (a group of two tiles) beside a window, caches alike
+EQUAL_STREAMS_CHUNKS = [(40, 256, 256), (2, 256, 256), (17, 256, 256)]
+
+
+@pytest.mark.parametrize("streams", [EQUAL_STREAMS, EQUAL_STREAMS_CHUNKS], ids=["windows", "chunks"])
+def test_control_every_stream_reads_stream0_kv_cache(streams):
+    print(f"\n[control] K/V cache of stream 0 read by every stream {streams}", flush=True)
     for field in ("k", "v"):
-        rnd = workloads.Round(0, "cuda", n_conv=0, n_attn=1, streams=EQUAL_STREAMS,
+        rnd = workloads.Round(0, "cuda", n_conv=0, n_attn=1, streams=streams,
                               with_logits=False)
         rb, out = run_round(rnd, with_argmax=False)
         rows = list(range(rnd.R))
