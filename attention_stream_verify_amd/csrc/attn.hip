@@ -18,9 +18,10 @@
 // one a wave, that walk the split's keys together through one shared ring
 // (attn_group below).
 //
-// Per 32-key sub-block, on the bf16 16x16x32 MFMA (fp32 accumulate):
-//   S^T[key][q]  = K[key][:] . Q[q][:]        (2 key tiles x 2 d-steps)
-//   O^T[d][q]   += V^T[d][key] P^T[key][q]    (4 d tiles, P split hi + lo)
+// Per 32-key sub-block, on the 16x16x32 MFMA (fp32 accumulate):
+//   S^T[key][q]  = K[key][:] . Q[q][:]        (bf16; 2 key tiles x 2 d-steps)
+//   O^T[d][q]   += V^T[d][key] P^T[key][q]    (4 d tiles: bf16 with P split
+//                                              hi + lo, or fp16 for groups)
 // K rows are key-major in HBM, V is d-major inside 32-key blocks; each
 // operand is one conflict-free 16-byte LDS read.
 //
@@ -30,6 +31,16 @@
 // P operand of the PV MFMA, whose V operand is V^T[d][8G..8G+7]. P is fed
 // as two bf16 parts (hi = the top 16 bits of the fp32 weight, lo = the
 // rest) so the partials keep ~16 bits of the weights, not bf16's 8.
+//
+// Group items run the PV product on the fp16 MFMA instead, one MFMA a d
+// tile: each wave rewrites its quarter of every V sub-block in LDS as fp16
+// under a running power-of-2 scale of its d tile (exact for every finite
+// bf16 value down to 2^-32 of the largest seen), and the weights are
+// rounded to fp16 (11 bits: relative error at most 2^-11 each, the same
+// rounded weights in l and in o). This halves the MFMAs of the product,
+// where the chunks' arithmetic goes, at a cost in the partials' error:
+// about 5e-4 of a record's largest |o| at most on the test workloads, where
+// bf16 hi + lo stays near 3e-5.
 //
 // Bits depend only on the item's own stream: the split plan and the grouping
 // of its tiles come from the stream's rows and keys, each item writes its
@@ -49,6 +60,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// The fp16 form of the same product, for group items whose V sub-block fits
+// fp16 exactly (see group_convert).
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -75,6 +93,7 @@ struct WaveState {
   f32x4 acc[4][QPW];
   f32x4 l[QPW];
   float mref[QPW], nmc[QPW], thr[QPW], ms[QPW];
+  uint32_t ev;  // group items: byte dt = the V scale exponent of d tile dt + 112
 };
 
 // Loop-invariant operands of accumulate, each held in registers: a ones
@@ -99,6 +118,11 @@ __device__ __forceinline__ Consts make_consts() {
 }
 
 constexpr float kLazy = 8.f;  // weights stay <= 2^8 between rebases
+// Group items round the weights to fp16 taken 2^7 times their value (at
+// most 2^15 then): fp16's normal range then holds every weight down to
+// 2^-21 of the base with its full 11 bits, below which a weight keeps bits
+// down to 2^-31 of the base only.
+constexpr int kPShift16 = 7;
 
 // Each wave streams its own 32-key sub-blocks (the item's sub-blocks w,
 // w+4, w+8, ... for wave w) through a private two-slot LDS ring filled by
@@ -184,8 +208,10 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 
 // Rebase q tile u (wave-uniform, rare): every column moves its base up to
 // its max score so far (smax: the lane's max of this sub-block); x * 1.0f
-// leaves the bits of columns that do not move unchanged.
-template <int QPW>
+// leaves the bits of columns that do not move unchanged. PSHIFT: weights
+// are taken 2^PSHIFT times their value at the base (l and o alike, so o is
+// unchanged and l is divided back at the end).
+template <int QPW, int PSHIFT = 0>
 __device__ __forceinline__ void rebase(WaveState<QPW>& st, int u, float smax) {
   const float c = kScale * kLog2e;
   const float ninf = -__builtin_inff();
@@ -193,7 +219,7 @@ __device__ __forceinline__ void rebase(WaveState<QPW>& st, int u, float smax) {
   const float mn = fmaxf(st.mref[u], mx);
   const float alpha = (mn > st.mref[u]) ? exp2_((st.mref[u] - mn) * c) : 1.f;
   st.mref[u] = mn;
-  st.nmc[u] = (mn == ninf) ? 0.f : -mn * c;
+  st.nmc[u] = (mn == ninf) ? 0.f : -mn * c + float(PSHIFT);
   st.thr[u] = mn + kLazy / c;
   st.l[u] *= alpha;
 #pragma unroll
@@ -238,6 +264,29 @@ __device__ __forceinline__ void accumulate(WaveState<QPW>& st, int u, float (&p)
   st.l[u] = mfma(kc.ones, lo, st.l[u]);
 }
 
+// accumulate for a sub-block whose V operands hold fp16: the weights are
+// rounded to fp16 (one v_cvt_pk_f16_f32 a pair, relative error <= 2^-11),
+// and the same rounded weights go through one PV MFMA per d tile and one l
+// MFMA, so o = acc / l stays an exact weighted mean of V under the rounded
+// weights.
+template <int QPW>
+__device__ __forceinline__ void accumulate16(WaveState<QPW>& st, int u, float (&p)[8],
+                                             const u32x4 (&v)[4], const u32x4& ones16) {
+  const float c = kScale * kLog2e;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) p[jj] = exp2_(__builtin_fmaf(p[jj], c, st.nmc[u]));
+  u32x4 ph;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const f32x2 f = {p[2 * w], p[2 * w + 1]};
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+    ph[w] = h;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) st.acc[dt][u] = mfma16(v[dt], ph, st.acc[dt][u]);
+  st.l[u] = mfma16(ones16, ph, st.l[u]);
+}
+
 // Scores of q tile u over the sub-block's 32 keys: lane (G, c) gets, for q
 // column c, keys 8G .. 8G+7 (the first four from key tile 0, the last four
 // from key tile 1). EDGE: keys at or past the column's visible count are
@@ -271,16 +320,20 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return uint32_t(size_t((__attribute__((address_space(3))) const char*)(p)));
 }
 
-// K operands: rows at a0 and a1 (d-steps 0 and 1), key tile 1 512 bytes on
-__device__ __forceinline__ void lds_read_k(u32x4 (&k)[4], uint32_t a0, uint32_t a1) {
+// K operands: rows at a0 and a1 (d-steps 0 and 1), key tile 1 512 bytes on;
+// with them the 16 bytes at aq (this lane's part of the next sub-block's
+// quarter, which the wave converts), all under one wait.
+__device__ __forceinline__ void lds_read_k_q(u32x4 (&k)[4], u32x4& q, uint32_t a0, uint32_t a1,
+                                             uint32_t aq) {
   asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %5\n\t"
-      "ds_read_b128 %2, %4 offset:512\n\t"
-      "ds_read_b128 %3, %5 offset:512\n\t"
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b128 %1, %6\n\t"
+      "ds_read_b128 %2, %5 offset:512\n\t"
+      "ds_read_b128 %3, %6 offset:512\n\t"
+      "ds_read_b128 %4, %7\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
-      : "v"(a0), "v"(a1)
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(q)
+      : "v"(a0), "v"(a1), "v"(aq)
       : "memory");
 }
 
@@ -297,6 +350,118 @@ __device__ __forceinline__ void lds_read_v(u32x4 (&v)[4], uint32_t a) {
       : "memory");
 }
 
+// Largest u32 over the wave: DPP within rows of 16 lanes, then across rows.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+  auto dmax = [](uint32_t v, uint32_t o) { return v > o ? v : o; };
+  x = dmax(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0xB1, 0xF, 0xF, false)));   // lane ^ 1
+  x = dmax(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x4E, 0xF, 0xF, false)));   // lane ^ 2
+  x = dmax(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x141, 0xF, 0xF, false)));  // 7 - i in 8
+  x = dmax(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x140, 0xF, 0xF, false)));  // 15 - i
+  x = umax_xor16(x);
+  x = umax_xor32(x);
+  return uint32_t(__builtin_amdgcn_readfirstlane(int(x)));
+}
+
+// Wave w's pass over its own quarter of a landed sub-block (d tile w of V,
+// all 32 keys: the 16 bytes each lane loaded itself), before the block
+// barrier. V past the key count is zeroed; the quarter is then scaled by 2^e
+// and rewritten in place as fp16. e is the wave's running exponent erun,
+// lowered whenever the quarter's largest finite magnitude needs it: with
+// E its bf16 exponent field, 142 - E puts that magnitude below 2^16, so
+// every finite value lands on an fp16 number exactly (8 significant bits)
+// unless it falls below 2^-17 after scaling, 2^-32 of the largest, where
+// it keeps bits down to 2^-24. Inf and NaN stay Inf and NaN. e + 112 goes to
+// byte w of the slot's exponent word.
+//
+// convert_quarter takes the 16 bytes already read from LDS address a, where
+// it writes them back.
+__device__ __forceinline__ void convert_quarter(u32x4 x, uint32_t a, uint32_t word_addr, int wave,
+                                                int lane, int kb, int keys, int& erun) {
+  if (kb + 32 > keys) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) x[w] = zero_past(x[w], kb + 8 * (lane >> 4) + 2 * w, keys);
+  }
+  u16x2 mx = {0, 0};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t m = x[w] & 0x7FFF7FFFu;
+    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, m));
+  }
+  // erun only falls: when every magnitude fits the current exponent (bf16
+  // exponent field at most 142 - erun), min(erun, 142 - E) is erun, and the
+  // exact largest magnitude (a cross-lane max) is needed only otherwise
+  const uint32_t lm = mx[0] > mx[1] ? mx[0] : mx[1];
+  if (__any(lm >= (uint32_t(143 - erun) << 7))) {
+    uint32_t top = wave_umax(lm);
+    if (top >= 0x7F80u) {  // Inf or NaN present: the largest finite magnitude
+      uint32_t f = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = x[w] & 0x7FFFu, hi = (x[w] >> 16) & 0x7FFFu;
+        f = (lo < 0x7F80u && lo > f) ? lo : f;
+        f = (hi < 0x7F80u && hi > f) ? hi : f;
+      }
+      top = wave_umax(f);
+    }
+    erun = min(erun, 142 - int(top >> 7));  // in [-112, 142]
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t y = x[w];
+    const f32x2 f = {__builtin_amdgcn_ldexpf(__uint_as_float(y << 16), erun),
+                     __builtin_amdgcn_ldexpf(__uint_as_float(y & 0xFFFF0000u), erun)};
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+    x[w] = h;
+  }
+  const uint32_t eb = uint32_t(erun + 112);
+  asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(x) : "memory");
+  asm volatile("ds_write_b8 %0, %1" ::"v"(word_addr + uint32_t(wave)), "v"(eb) : "memory");
+}
+
+// LDS address of this lane's 16 bytes of the wave's quarter of a slot.
+__device__ __forceinline__ uint32_t quarter_addr(const char* slot, int wave, int lane) {
+  return lds_addr(slot) + 4096 + uint32_t(wave * 1024 + lane * 16);
+}
+
+__device__ __forceinline__ void group_convert(const char* slot, uint32_t word_addr, int wave,
+                                              int lane, int kb, int keys, int& erun) {
+  const uint32_t a = quarter_addr(slot, wave, lane);
+  u32x4 x;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(x) : "v"(a) : "memory");
+  convert_quarter(x, a, word_addr, wave, lane, kb, keys, erun);
+}
+
+// The next sub-block's quarter a wave converts while it computes the current
+// one: its LDS address (this lane's 16 bytes), its slot's exponent word, its
+// first key, and the wave's running exponent.
+struct NextQuarter {
+  uint32_t a, word_addr;
+  int kb, wave;
+  int* erun;
+};
+
+// The exponent word of a slot (after the barrier), the same for the whole
+// wave.
+__device__ __forceinline__ uint32_t group_word(uint32_t word_addr) {
+  uint32_t f;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(f) : "v"(word_addr) : "memory");
+  return uint32_t(__builtin_amdgcn_readfirstlane(int(f)));
+}
+
+// How a sub-block's V operands are read and fed to the PV product.
+//  kVPrivate: a single-tile item's private slot, plain LDS reads, bf16 V;
+//    V past the key count is zeroed in registers (EDGE).
+//  kVGroupF16: the shared ring of a group item, opaque reads; group_convert
+//    has zeroed V past the key count and rewritten every d tile as fp16,
+//    scaled by 2^e (e from the slot's exponent word vword); the PV and l
+//    products run on the fp16 MFMA (accumulate16).
+enum { kVPrivate = 0, kVGroupF16 = 1 };
+
+// Exponent e of d tile dt in an exponent word (bytes hold e + 112).
+__device__ __forceinline__ int vexp(uint32_t word, int dt) {
+  return int((word >> (8 * dt)) & 0xFFu) - 112;
+}
+
 // One 32-key sub-block for QPW q tiles. The scores of every q tile come
 // first, with the lane's max score of each; one wave-uniform test then says
 // whether any score exceeds its column's threshold (or this is the wave's
@@ -304,13 +469,20 @@ __device__ __forceinline__ void lds_read_v(u32x4 (&v)[4], uint32_t a) {
 // and accumulation of every q tile follow the join, in place over the
 // scores, so nothing is computed twice and the accumulators stay in their
 // registers on both paths. EDGE: the sub-block reaches past some row's
-// causal limit or past the key count, so scores are masked and V past the
-// key count is zeroed.
-template <int QPW, bool EDGE, bool OPAQUE = false>
+// causal limit or past the key count, so scores are masked (and, for
+// kVPrivate, V past the key count is zeroed). vword: for kVGroupF16, the
+// slot's exponent word; when it differs from the wave's, the accumulators
+// of each d tile move to the new scale (2^(e_new - e_old), exact) on the
+// rebase path. nxt (kVGroupF16): the next sub-block's quarter, read with
+// the K operands and converted after the products, so that its LDS round
+// trip and arithmetic overlap this sub-block's work.
+template <int QPW, bool EDGE, int VMODE = kVPrivate>
 __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, bool first,
                                           const u32x4 (&qop)[QPW][2], const int (&nq)[QPW],
                                           WaveState<QPW>& st, int lane, uint32_t kr0,
-                                          const Consts& kc) {
+                                          const Consts& kc, uint32_t vword = 0,
+                                          const NextQuarter& nxt = NextQuarter{}) {
+  constexpr bool OPAQUE = VMODE != kVPrivate;
   const int G = lane >> 4;
   auto rd = [&](uint32_t off) { return *reinterpret_cast<const u32x4*>(sub + off); };
   // d-step 1 flips bit 2 of the chunk index; computed here by an opaque
@@ -318,9 +490,10 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, boo
   uint32_t kr1;
   asm volatile("v_xor_b32 %0, 64, %1" : "=v"(kr1) : "v"(kr0));
   u32x4 k[4];
+  u32x4 xq;  // kVGroupF16: the next quarter
   if constexpr (OPAQUE) {
     const uint32_t base = lds_addr(sub);
-    lds_read_k(k, base + kr0, base + kr1);
+    lds_read_k_q(k, xq, base + kr0, base + kr1, nxt.a);
   } else {
     k[0] = rd(kr0);
     k[1] = rd(kr1);
@@ -338,9 +511,22 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, boo
     st.ms[u] = __builtin_elementwise_maximum(st.ms[u], smax[u]);
     over |= smax[u] > st.thr[u];
   }
-  if (first || __any(over)) {
+  bool rescale = false;
+  if constexpr (VMODE == kVGroupF16) rescale = vword != st.ev;
+  if (first || rescale || __any(over)) {
 #pragma unroll
-    for (int u = 0; u < QPW; ++u) rebase<QPW>(st, u, smax[u]);
+    for (int u = 0; u < QPW; ++u) rebase<QPW, (VMODE == kVGroupF16) ? kPShift16 : 0>(st, u, smax[u]);
+    if constexpr (VMODE == kVGroupF16) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int de = vexp(vword, dt) - vexp(st.ev, dt);
+#pragma unroll
+        for (int u = 0; u < QPW; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.acc[dt][u][e] = __builtin_amdgcn_ldexpf(st.acc[dt][u][e], de);
+      }
+      st.ev = vword;
+    }
   }
   // V operands only now: K is dead, so the two are never live together
   u32x4 v[4];
@@ -350,7 +536,7 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, boo
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) v[dt] = rd(4096 + dt * 1024 + lane * 16);
   }
-  if constexpr (EDGE) {
+  if constexpr (VMODE == kVPrivate && EDGE) {
     if (kb + 32 > keys) {  // slots past the key count may hold anything
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -358,18 +544,34 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, boo
         for (int w = 0; w < 4; ++w) v[dt][w] = zero_past(v[dt][w], kb + 8 * G + 2 * w, keys);
     }
   }
+  if constexpr (VMODE == kVGroupF16) {
+    uint32_t o16 = 0x3C003C00u;  // fp16 (1, 1), in a register (see Consts)
+    asm volatile("" : "+v"(o16));
+    const u32x4 ones16 = u32x4{o16, o16, o16, o16};
 #pragma unroll
-  for (int u = 0; u < QPW; ++u) accumulate<QPW>(st, u, sc[u], v, kc);
-  // Schedule: q tile 0's weights first, then every MFMA of the PV and l
-  // products followed by VALU work of the later q tiles. Left alone, the
-  // compiler puts all weights before all MFMAs, and the matrix core idles
-  // while the wave computes weights and the other way round.
-  if constexpr (QPW > 1) {
-    __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);  // VALU: q tile 0
+    for (int u = 0; u < QPW; ++u) accumulate16<QPW>(st, u, sc[u], v, ones16);
+    // as below, with five MFMAs and 20 VALU instructions a q tile
+    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
 #pragma unroll
-    for (int i = 0; i < 10 * QPW; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+    for (int i = 0; i < 5 * QPW; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+    convert_quarter(xq, nxt.a, nxt.word_addr, nxt.wave, lane, nxt.kb, keys, *nxt.erun);
+  } else {
+#pragma unroll
+    for (int u = 0; u < QPW; ++u) accumulate<QPW>(st, u, sc[u], v, kc);
+    // Schedule: q tile 0's weights first, then every MFMA of the PV and l
+    // products followed by VALU work of the later q tiles. Left alone, the
+    // compiler puts all weights before all MFMAs, and the matrix core idles
+    // while the wave computes weights and the other way round.
+    if constexpr (QPW > 1) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);  // VALU: q tile 0
+#pragma unroll
+      for (int i = 0; i < 10 * QPW; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+      }
     }
   }
 }
@@ -630,7 +832,8 @@ template <int AUX>
 __device__ __forceinline__ void attn_group(const TableView& tv, int layer,
                                            const uint16_t* __restrict__ Q, float* __restrict__ po,
                                            float* __restrict__ pml, const asv_work wk,
-                                           char* __restrict__ ringA, char* __restrict__ ringB) {
+                                           char* __restrict__ ringA, char* __restrict__ ringB,
+                                           uint32_t* __restrict__ vword) {
   constexpr int QPW = 4;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -659,6 +862,7 @@ __device__ __forceinline__ void attn_group(const TableView& tv, int layer,
   const Consts kc = make_consts();
 
   WaveState<QPW> st;
+  st.ev = 0x70707070u;  // e = 0 (the first sub-block takes the rebase path)
   u32x4 qop[QPW][2];
   int nq[QPW];
   const float ninf = -__builtin_inff();
@@ -703,13 +907,36 @@ __device__ __forceinline__ void attn_group(const TableView& tv, int layer,
   // retire first), then the barrier says every wave's have, and that every
   // wave is done with sub-block i - 1, whose slot is refilled with sub-block
   // i + kGroupSlots - 1 before sub-block i is computed.
+  const uint32_t word0 = lds_addr(reinterpret_cast<const char*>(vword));
+  int erun = 142;  // this wave's V scale exponent (d tile `wave`); only falls
+  // sub-block 0's quarter now; sub-block i + 1's while sub-block i is
+  // computed (its loads have landed before barrier i)
+  group_convert(slot(0), word0, wave, lane, k0, S.keys, erun);
   auto step = [&](int i) -> const char* {
-    if (i + kGroupSlots - 2 < nb) wait_vm<2 * (kGroupSlots - 2)>();
+    if (i + kGroupSlots - 2 < nb) wait_vm<2 * (kGroupSlots - 3)>();
     else wait_vm<0>();
+    const int s = i & (kGroupSlots - 1);
     ring_barrier();
     const int nx = i + kGroupSlots - 1;
     if (nx < nb) issue_quarter<AUX>(slot(nx & (kGroupSlots - 1)), Kh, Vh, k0 + 32 * nx, koff, voff, wave);
-    return slot(i & (kGroupSlots - 1));
+    return slot(s);
+  };
+  // sub-block i of the slot just returned by step(i), with its exponent
+  // word; the quarter of sub-block i + 1 is converted meanwhile (after the
+  // last sub-block that is a spare slot with no load in flight: the
+  // conversion is harmless there)
+  auto run = [&](auto edge, const char* cur, int i) {
+    constexpr bool E = decltype(edge)::value;
+    const int sn = (i + 1) & (kGroupSlots - 1);
+    const NextQuarter nxt{quarter_addr(slot(sn), wave, lane), word0 + 4 * sn, k0 + 32 * (i + 1),
+                          wave, &erun};
+    if (active) {
+      const uint32_t w = group_word(word0 + 4 * (i & (kGroupSlots - 1)));
+      sub_block<QPW, E, kVGroupF16>(cur, k0 + 32 * i, S.keys, i == 0, qop, nq, st, lane, kr0, kc,
+                                    w, nxt);
+    } else {
+      group_convert(slot(sn), nxt.word_addr, wave, lane, nxt.kb, S.keys, erun);
+    }
   };
   // interior sub-blocks: every row of the group sees all of their keys
   const int lim = n_first - 32 - k0;
@@ -717,13 +944,11 @@ __device__ __forceinline__ void attn_group(const TableView& tv, int layer,
   int i = 0;
   for (; i < n_in; ++i) {
     const char* cur = step(i);
-    if (active)
-      sub_block<QPW, false, true>(cur, k0 + 32 * i, S.keys, i == 0, qop, nq, st, lane, kr0, kc);
+    run(std::false_type{}, cur, i);
   }
   for (; i < nb; ++i) {
     const char* cur = step(i);
-    if (active)
-      sub_block<QPW, true, true>(cur, k0 + 32 * i, S.keys, i == 0, qop, nq, st, lane, kr0, kc);
+    run(std::true_type{}, cur, i);
   }
   if (!active) return;
 
@@ -742,12 +967,15 @@ __device__ __forceinline__ void attn_group(const TableView& tv, int layer,
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         f32x4 r;
+        const int ed = -vexp(st.ev, dt);  // back from the scale of d tile dt
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = (L > 0.f) ? st.acc[dt][u][e] / L : 0.f;
+        for (int e = 0; e < 4; ++e)
+          r[e] = (L > 0.f) ? __builtin_amdgcn_ldexpf(st.acc[dt][u][e] / L, ed) : 0.f;
         store16f(po + rec * ASV_HEAD_DIM + dt * 16 + 4 * G, r);
       }
       if (G == 0) {
-        const float lt = (mt == ninf) ? 0.f : L * exp2_((st.mref[u] - mt) * c);
+        const float lt =
+            (mt == ninf) ? 0.f : __builtin_amdgcn_ldexpf(L, -kPShift16) * exp2_((st.mref[u] - mt) * c);
         gstore(reinterpret_cast<float2*>(pml) + rec, make_float2((mt == ninf) ? ninf : mt * kScale, lt));
       }
     }
@@ -763,6 +991,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split(TableView tv, int laye
   // being loaded from the one being read; the fold reuses them afterwards
   __shared__ __attribute__((aligned(16))) char ringA[kWaves * kSubBytes];
   __shared__ __attribute__((aligned(16))) char ringB[kWaves * kSubBytes];
+  __shared__ uint32_t vword[kGroupSlots];  // group items: V exponents a slot
   const asv_work wk = uniform(cload(tv.work + blockIdx.x));
   const asv_tile T = uniform(cload(tv.tiles + wk.tile));
   const int nqt = (T.nrows + 3) >> 2;
@@ -775,8 +1004,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split(TableView tv, int laye
     // (the last aside) hold 16 rows, so a round that has them launches this
     // instance
     if (wk.ntiles > 1) {
-      if (once) return attn_group<kStream>(tv, layer, Q, po, pml, wk, ringA, ringB);
-      return attn_group<0>(tv, layer, Q, po, pml, wk, ringA, ringB);
+      if (once) return attn_group<kStream>(tv, layer, Q, po, pml, wk, ringA, ringB, vword);
+      return attn_group<0>(tv, layer, Q, po, pml, wk, ringA, ringB, vword);
     }
     if (nqt == 4) {
       if (once) return attn_item<4, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB);
