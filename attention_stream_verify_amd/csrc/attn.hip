@@ -322,18 +322,20 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 
 // K operands: rows at a0 and a1 (d-steps 0 and 1), key tile 1 512 bytes on;
 // with them the 16 bytes at aq (this lane's part of the next sub-block's
-// quarter, which the wave converts), all under one wait.
-__device__ __forceinline__ void lds_read_k_q(u32x4 (&k)[4], u32x4& q, uint32_t a0, uint32_t a1,
-                                             uint32_t aq) {
+// quarter, which the wave converts) and the word at aw (the slot's exponent
+// word), all under one wait.
+__device__ __forceinline__ void lds_read_k_q(u32x4 (&k)[4], u32x4& q, uint32_t& w, uint32_t a0,
+                                             uint32_t a1, uint32_t aq, uint32_t aw) {
   asm volatile(
-      "ds_read_b128 %0, %5\n\t"
-      "ds_read_b128 %1, %6\n\t"
-      "ds_read_b128 %2, %5 offset:512\n\t"
-      "ds_read_b128 %3, %6 offset:512\n\t"
-      "ds_read_b128 %4, %7\n\t"
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b128 %2, %6 offset:512\n\t"
+      "ds_read_b128 %3, %7 offset:512\n\t"
+      "ds_read_b128 %4, %8\n\t"
+      "ds_read_b32 %5, %9\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(q)
-      : "v"(a0), "v"(a1), "v"(aq)
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(q), "=&v"(w)
+      : "v"(a0), "v"(a1), "v"(aq), "v"(aw)
       : "memory");
 }
 
@@ -365,33 +367,56 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
 // Wave w's pass over its own quarter of a landed sub-block (d tile w of V,
 // all 32 keys: the 16 bytes each lane loaded itself), before the block
 // barrier. V past the key count is zeroed; the quarter is then scaled by 2^e
-// and rewritten in place as fp16. e is the wave's running exponent erun,
-// lowered whenever the quarter's largest finite magnitude needs it: with
-// E its bf16 exponent field, 142 - E puts that magnitude below 2^16, so
-// every finite value lands on an fp16 number exactly (8 significant bits)
-// unless it falls below 2^-17 after scaling, 2^-32 of the largest, where
-// it keeps bits down to 2^-24. Inf and NaN stay Inf and NaN. e + 112 goes to
+// and rewritten in place as fp16. e is the wave's exponent for its d tile,
+// which follows the quarters' largest finite magnitudes: with E the bf16
+// exponent field of a quarter's largest, 142 - E puts it below 2^16. e is
+// lowered to that when the quarter does not fit, and raised to it (at most
+// 64 above the lowest e of the item, so the accumulators cannot overflow
+// when they follow) when every magnitude of the quarter is below 2^-8 of
+// what e allows; otherwise it stays. Every finite value so lands on an fp16
+// number exactly (8 significant bits) unless it falls below 2^-14 after
+// scaling, which is 2^-22 of its quarter's largest or less (unless the cap
+// held e down).
+// When the quarter fits the current e (the common case) the conversion is
+// integer arithmetic on the bf16 bits: magnitude minus (112 - e) << 7,
+// saturating at zero, shifted left by 3, with the sign put back; values
+// below 2^-14 after scaling then come out zero or off by less than 2^-14.
+// Otherwise (e moves, or Inf or NaN present, or e > 112) it goes through
+// fp32 (v_ldexp_f32, then v_cvt_pk_f16_f32), which keeps bits down to
+// 2^-24 after scaling, and Inf and NaN stay Inf and NaN. e + 112 goes to
 // byte w of the slot's exponent word.
 //
 // convert_quarter takes the 16 bytes already read from LDS address a, where
 // it writes them back.
+// A wave's V exponent for its d tile, and the lowest it has taken in the item.
+struct VScale {
+  int e = 142, emin = 142;
+};
+
 __device__ __forceinline__ void convert_quarter(u32x4 x, uint32_t a, uint32_t word_addr, int wave,
-                                                int lane, int kb, int keys, int& erun) {
+                                                int lane, int kb, int keys, VScale& vs) {
   if (kb + 32 > keys) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) x[w] = zero_past(x[w], kb + 8 * (lane >> 4) + 2 * w, keys);
   }
   u16x2 mx = {0, 0};
+  u16x2 mag[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const uint32_t m = x[w] & 0x7FFF7FFFu;
-    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, m));
+    mag[w] = __builtin_bit_cast(u16x2, m);
+    mx = __builtin_elementwise_max(mx, mag[w]);
   }
-  // erun only falls: when every magnitude fits the current exponent (bf16
-  // exponent field at most 142 - erun), min(erun, 142 - E) is erun, and the
-  // exact largest magnitude (a cross-lane max) is needed only otherwise
+  // the exact largest magnitude (a cross-lane max) is needed only when e
+  // must fall (a magnitude with exponent field above 142 - e) or may rise
+  // (every exponent field below 135 - e)
+  const int erun = vs.e;
   const uint32_t lm = mx[0] > mx[1] ? mx[0] : mx[1];
-  if (__any(lm >= (uint32_t(143 - erun) << 7))) {
+  const uint32_t lim = uint32_t(143 - erun) << 7;
+  const bool lower = __any(lm >= lim);
+  const bool raise = !lower && !__any(lm >= (lim > (8u << 7) ? lim - (8u << 7) : 0u));
+  bool moved = false;
+  if (lower || raise) {
     uint32_t top = wave_umax(lm);
     if (top >= 0x7F80u) {  // Inf or NaN present: the largest finite magnitude
       uint32_t f = 0;
@@ -403,17 +428,34 @@ __device__ __forceinline__ void convert_quarter(u32x4 x, uint32_t a, uint32_t wo
       }
       top = wave_umax(f);
     }
-    erun = min(erun, 142 - int(top >> 7));  // in [-112, 142]
+    if (top != 0) {  // an all-zero quarter leaves e alone
+      const int en = 142 - int(top >> 7);  // in [-112, 142]
+      vs.e = lower ? min(erun, en) : max(erun, min(en, vs.emin + 64));
+      vs.emin = min(vs.emin, vs.e);
+    }
+    moved = true;
   }
+  const int e = vs.e;
+  if (!moved && e <= 112) {
+    const uint32_t b = uint32_t(112 - e) << 7;
+    const u16x2 bias = __builtin_bit_cast(u16x2, b | (b << 16));
+    const u16x2 three = {3, 3};
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t y = x[w];
-    const f32x2 f = {__builtin_amdgcn_ldexpf(__uint_as_float(y << 16), erun),
-                     __builtin_amdgcn_ldexpf(__uint_as_float(y & 0xFFFF0000u), erun)};
-    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
-    x[w] = h;
+    for (int w = 0; w < 4; ++w) {
+      const u16x2 t = __builtin_elementwise_sub_sat(mag[w], bias) << three;
+      x[w] = (x[w] & 0x80008000u) | __builtin_bit_cast(uint32_t, t);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t y = x[w];
+      const f32x2 f = {__builtin_amdgcn_ldexpf(__uint_as_float(y << 16), e),
+                       __builtin_amdgcn_ldexpf(__uint_as_float(y & 0xFFFF0000u), e)};
+      const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+      x[w] = h;
+    }
   }
-  const uint32_t eb = uint32_t(erun + 112);
+  const uint32_t eb = uint32_t(e + 112);
   asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(x) : "memory");
   asm volatile("ds_write_b8 %0, %1" ::"v"(word_addr + uint32_t(wave)), "v"(eb) : "memory");
 }
@@ -424,29 +466,24 @@ __device__ __forceinline__ uint32_t quarter_addr(const char* slot, int wave, int
 }
 
 __device__ __forceinline__ void group_convert(const char* slot, uint32_t word_addr, int wave,
-                                              int lane, int kb, int keys, int& erun) {
+                                              int lane, int kb, int keys, VScale& vs) {
   const uint32_t a = quarter_addr(slot, wave, lane);
   u32x4 x;
   asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(x) : "v"(a) : "memory");
-  convert_quarter(x, a, word_addr, wave, lane, kb, keys, erun);
+  convert_quarter(x, a, word_addr, wave, lane, kb, keys, vs);
 }
 
-// The next sub-block's quarter a wave converts while it computes the current
-// one: its LDS address (this lane's 16 bytes), its slot's exponent word, its
-// first key, and the wave's running exponent.
+// What a group sub-block reads and writes beside its own operands: the
+// current slot's exponent word, and the next sub-block's quarter, which the
+// wave converts while it computes the current one (its LDS address, this
+// lane's 16 bytes; its slot's exponent word; its first key; the wave's
+// V exponent).
 struct NextQuarter {
+  uint32_t word_cur;
   uint32_t a, word_addr;
   int kb, wave;
-  int* erun;
+  VScale* vs;
 };
-
-// The exponent word of a slot (after the barrier), the same for the whole
-// wave.
-__device__ __forceinline__ uint32_t group_word(uint32_t word_addr) {
-  uint32_t f;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(f) : "v"(word_addr) : "memory");
-  return uint32_t(__builtin_amdgcn_readfirstlane(int(f)));
-}
 
 // How a sub-block's V operands are read and fed to the PV product.
 //  kVPrivate: a single-tile item's private slot, plain LDS reads, bf16 V;
@@ -470,18 +507,17 @@ __device__ __forceinline__ int vexp(uint32_t word, int dt) {
 // scores, so nothing is computed twice and the accumulators stay in their
 // registers on both paths. EDGE: the sub-block reaches past some row's
 // causal limit or past the key count, so scores are masked (and, for
-// kVPrivate, V past the key count is zeroed). vword: for kVGroupF16, the
-// slot's exponent word; when it differs from the wave's, the accumulators
-// of each d tile move to the new scale (2^(e_new - e_old), exact) on the
-// rebase path. nxt (kVGroupF16): the next sub-block's quarter, read with
-// the K operands and converted after the products, so that its LDS round
-// trip and arithmetic overlap this sub-block's work.
+// kVPrivate, V past the key count is zeroed). nxt (kVGroupF16): the slot's
+// exponent word, read with the K operands (when it differs from the wave's,
+// the accumulators of each d tile move to the new scale, 2^(e_new - e_old),
+// exactly, on the rebase path), and the next sub-block's quarter, read with
+// them too and converted before the products, so that its LDS write has
+// landed by the next barrier.
 template <int QPW, bool EDGE, int VMODE = kVPrivate>
 __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, bool first,
                                           const u32x4 (&qop)[QPW][2], const int (&nq)[QPW],
                                           WaveState<QPW>& st, int lane, uint32_t kr0,
-                                          const Consts& kc, uint32_t vword = 0,
-                                          const NextQuarter& nxt = NextQuarter{}) {
+                                          const Consts& kc, const NextQuarter& nxt = NextQuarter{}) {
   constexpr bool OPAQUE = VMODE != kVPrivate;
   const int G = lane >> 4;
   auto rd = [&](uint32_t off) { return *reinterpret_cast<const u32x4*>(sub + off); };
@@ -490,10 +526,14 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, boo
   uint32_t kr1;
   asm volatile("v_xor_b32 %0, 64, %1" : "=v"(kr1) : "v"(kr0));
   u32x4 k[4];
-  u32x4 xq;  // kVGroupF16: the next quarter
+  uint32_t vword = 0;  // kVGroupF16: the slot's exponent word
   if constexpr (OPAQUE) {
     const uint32_t base = lds_addr(sub);
-    lds_read_k_q(k, xq, base + kr0, base + kr1, nxt.a);
+    u32x4 xq;
+    uint32_t wv;
+    lds_read_k_q(k, xq, wv, base + kr0, base + kr1, nxt.a, nxt.word_cur);
+    vword = uint32_t(__builtin_amdgcn_readfirstlane(int(wv)));
+    convert_quarter(xq, nxt.a, nxt.word_addr, nxt.wave, lane, nxt.kb, keys, *nxt.vs);
   } else {
     k[0] = rd(kr0);
     k[1] = rd(kr1);
@@ -557,7 +597,6 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, boo
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
-    convert_quarter(xq, nxt.a, nxt.word_addr, nxt.wave, lane, nxt.kb, keys, *nxt.erun);
   } else {
 #pragma unroll
     for (int u = 0; u < QPW; ++u) accumulate<QPW>(st, u, sc[u], v, kc);
@@ -908,10 +947,10 @@ __device__ __forceinline__ void attn_group(const TableView& tv, int layer,
   // wave is done with sub-block i - 1, whose slot is refilled with sub-block
   // i + kGroupSlots - 1 before sub-block i is computed.
   const uint32_t word0 = lds_addr(reinterpret_cast<const char*>(vword));
-  int erun = 142;  // this wave's V scale exponent (d tile `wave`); only falls
+  VScale vsc;  // this wave's V exponent (d tile `wave`)
   // sub-block 0's quarter now; sub-block i + 1's while sub-block i is
   // computed (its loads have landed before barrier i)
-  group_convert(slot(0), word0, wave, lane, k0, S.keys, erun);
+  group_convert(slot(0), word0, wave, lane, k0, S.keys, vsc);
   auto step = [&](int i) -> const char* {
     if (i + kGroupSlots - 2 < nb) wait_vm<2 * (kGroupSlots - 3)>();
     else wait_vm<0>();
@@ -928,14 +967,14 @@ __device__ __forceinline__ void attn_group(const TableView& tv, int layer,
   auto run = [&](auto edge, const char* cur, int i) {
     constexpr bool E = decltype(edge)::value;
     const int sn = (i + 1) & (kGroupSlots - 1);
-    const NextQuarter nxt{quarter_addr(slot(sn), wave, lane), word0 + 4 * sn, k0 + 32 * (i + 1),
-                          wave, &erun};
+    const NextQuarter nxt{word0 + 4 * uint32_t(i & (kGroupSlots - 1)),
+                          quarter_addr(slot(sn), wave, lane), word0 + 4 * sn, k0 + 32 * (i + 1),
+                          wave, &vsc};
     if (active) {
-      const uint32_t w = group_word(word0 + 4 * (i & (kGroupSlots - 1)));
       sub_block<QPW, E, kVGroupF16>(cur, k0 + 32 * i, S.keys, i == 0, qop, nq, st, lane, kr0, kc,
-                                    w, nxt);
+                                    nxt);
     } else {
-      group_convert(slot(sn), nxt.word_addr, wave, lane, nxt.kb, S.keys, erun);
+      group_convert(slot(sn), nxt.word_addr, wave, lane, nxt.kb, S.keys, vsc);
     }
   };
   // interior sub-blocks: every row of the group sees all of their keys

@@ -2,9 +2,10 @@
 against exact scale invariance.
 
 A group item rewrites each 32-key V quarter (one 16-wide d tile) in LDS as
-fp16 scaled by 2^e, where e is a running per-d-tile exponent that keeps the
-largest finite magnitude seen below 2^16, and rounds the weights to fp16.
-These tests aim at what that design could get wrong:
+fp16 scaled by 2^e, where e is a per-d-tile exponent that follows the
+quarters' largest magnitudes (down at once when a quarter does not fit below
+2^16, up when a quarter is far below what e allows), and rounds the weights
+to fp16. These tests aim at what that design could get wrong:
 - V of any magnitude: scaling V by 2^s must scale every partial o and every
   merged output by exactly 2^s and leave m and l bit-identical (the kernel's
   scale moves by exactly -s, so the fp16 operands are the same bits);
@@ -12,7 +13,9 @@ These tests aim at what that design could get wrong:
   count, in l and in o;
 - d tiles of very different magnitudes, a scale that falls in the middle of
   an item, and whole zero sub-blocks at the start of an item: each d tile
-  must stay within 1e-3 of its own largest |o|.
+  must stay within 1e-3 of its own largest |o|;
+- a huge V value at a key of negligible weight: the scale must come back up
+  after its sub-block.
 """
 
 import numpy as np
@@ -143,3 +146,41 @@ def test_v_scales_per_d_tile():
                              "merged output")
     print(f"[fp16] per-d-tile scales: partial rel err {prel:.2e}, output rel err {orel:.2e}",
           flush=True)
+
+
+def test_v_outlier_with_negligible_weight():
+    """One V value 2^30 (d tile 0) at a key whose weight is about e^-40:
+    its sub-block's quarter takes a scale 2^-30 lower, and the next quarters
+    must take the scale back up, or every later value of that d tile would
+    keep only a few bits."""
+    streams = [(64, 3000, 3008)]
+    print(f"\n[fp16] V outlier at a negligible weight: {streams}", flush=True)
+    rnd = workloads.Round(0, "cuda", n_conv=0, n_attn=1, streams=streams, with_logits=False)
+    Q, ks, vs = rnd.attn[0]
+    q = Q.view(torch.bfloat16).float()
+    q[..., 0] = 4.0           # with k[100][0] = -80: 40 off every score of key 100
+    Q.copy_(q.to(torch.bfloat16).view(torch.int16))
+    k = ks[0].view(torch.bfloat16).float()
+    k[:, 100, 0] = -80.0
+    ks[0].copy_(k.to(torch.bfloat16).view(torch.int16))
+    v = workloads.v_logical(vs[0]).view(torch.bfloat16).float()
+    v[:, 100, 0:16] = 2.0 ** 30
+    vs[0].copy_(workloads.v_blocked(v.to(torch.bfloat16).view(torch.int16)))
+
+    rb, out = run_round(rnd, with_argmax=False)
+    t = otable.build(streams)
+    rows = list(range(t.n_rows))
+    Qh, Kh, Vh = oracle_attn_inputs(rnd, 0)
+    ref_o, ref_m, ref_l, _ = oattn.partials(t, Qh, Kh, Vh, rows=rows)
+    dense = oattn.attention(t, Qh, Kh, Vh, rows=rows)
+    po, pml = _partials(rb, out)
+    recs = [t.record(r, h, sp) for r in rows for h in range(32) for sp in range(t.row_nsplit(r))]
+    recs = np.asarray(recs, dtype=np.int64)
+    # the outlier must not dominate: the reference's d tile 0 stays small
+    assert np.abs(ref_o[recs, :16]).max() < 16.0
+    assert np.all(np.abs(pml[recs, 1] - ref_l[recs]) <= 1e-3 * ref_l[recs])
+    prel = _check_per_d_tile(po[recs], ref_o[recs], 1e-3, "partials")
+    g = bf16_to_f64(host_u16(out["o"][0]))[rows]
+    orel = _check_per_d_tile(g.reshape(-1, 64), dense[rows].reshape(-1, 64), 2.0 ** -8 + 1e-3,
+                             "merged output")
+    print(f"[fp16] V outlier: partial rel err {prel:.2e}, output rel err {orel:.2e}", flush=True)
