@@ -34,13 +34,13 @@
 //
 // Group items run the PV product on the fp16 MFMA instead, one MFMA a d
 // tile: each wave rewrites its quarter of every V sub-block in LDS as fp16
-// under a running power-of-2 scale of its d tile (exact for every finite
-// bf16 value down to 2^-32 of the largest seen), and the weights are
-// rounded to fp16 (11 bits: relative error at most 2^-11 each, the same
-// rounded weights in l and in o). This halves the MFMAs of the product,
-// where the chunks' arithmetic goes, at a cost in the partials' error:
-// about 5e-4 of a record's largest |o| at most on the test workloads, where
-// bf16 hi + lo stays near 3e-5.
+// under a power-of-2 scale of its d tile that follows the values' size
+// (exact for every finite bf16 value down to 2^-22 of its sub-block's
+// largest; convert_quarter), and the weights are rounded to fp16 (11 bits:
+// relative error at most 2^-11 each, the same rounded weights in l and in
+// o). This halves the MFMAs of the product, where the chunks' arithmetic
+// goes, at a cost in the partials' error: about 5e-4 of a record's largest
+// |o| at most on the test workloads, where bf16 hi + lo stays near 2e-5.
 //
 // Bits depend only on the item's own stream: the split plan and the grouping
 // of its tiles come from the stream's rows and keys, each item writes its
@@ -63,7 +63,7 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // The fp16 form of the same product, for group items whose V sub-block fits
-// fp16 exactly (see group_convert).
+// fp16 exactly (see convert_quarter).
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);

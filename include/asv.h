@@ -272,7 +272,7 @@ int asv_shared_conv(const asv_table_info* info, const void* dev_blob, int32_t la
  * to fp16 (11 bits, V scaled exactly into fp16 by a power of 2 per 16-wide
  * d tile) for longer streams (prompt chunks). Within 1e-3 of the record's
  * largest |o| and 1e-3 of l on the tested workloads (largest seen: 5e-4
- * for chunks, 3e-5 otherwise).
+ * for chunks, 2e-5 otherwise).
  *
  *   q         bf16 [n_rows][32][64], 16-byte aligned
  *   partials  float [info->partial_count * 66], 16-byte aligned: the o
