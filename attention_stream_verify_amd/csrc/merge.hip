@@ -15,20 +15,27 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Merge: one wave per (row, q head); lane d owns output dim d. Lanes first
-// run over the row's splits (lane j holds split t0 + j of a 64-split chunk)
-// to take M = max_t m_t, then compute each split's weight
-// w_t = e^(m_t - M) l_t in the lane that loaded it. A sequential pass in
-// split order, t = 0, 1, ..., then adds w_t (broadcast from its lane) to L
-// and w_t o_t[d] to the output; the o loads of successive splits are
-// independent, so they are in flight together. Empty splits (l = 0) take
-// no part; a NaN partial propagates.
+// Merge: one wave per (row, group of 4 q heads); the 16 lanes 16j..16j+15
+// serve head 4g + j, lane 16j + c output dims 4c..4c+3, so each split's o
+// records of the four heads (1 KB, contiguous) come in one 16-byte load a
+// lane. First each head's lanes take M = max_t m_t over its non-empty
+// splits (lane c looks at splits c, c + 16, ...; a max over the 16 lanes
+// follows). Then one pass in split order, t = 0, 1, ..., adds
+// w_t = e^(m_t - M) l_t to L and w_t o_t[d] to the output, each lane
+// computing w_t from its head's (m_t, l_t) (the same 8 bytes for the 16
+// lanes); the loads of 8 successive splits are in flight together. Empty
+// splits (l = 0) take no part; a NaN partial propagates. The arithmetic of
+// every output element, and its order, is that of one lane per element.
 constexpr int kMergeWaves = 4;
+constexpr int kHeadsPerWave = 4;
 
-__device__ __forceinline__ float wave_max(float x) {
-  x = max_xor32(max_xor16(x));
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 16));
+// Max over the 16 lanes of a row of the wave (DPP within rows).
+__device__ __forceinline__ float row16_max(float x) {
+  auto dmax = [](float v, int ctrl_v) { return fmaxf(v, __int_as_float(ctrl_v)); };
+  x = dmax(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // ^1
+  x = dmax(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // ^2
+  x = dmax(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)); // 7-i
+  x = dmax(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)); // 15-i
   return x;
 }
 
@@ -36,11 +43,13 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_rows(TableView tv,
                                                                const float* __restrict__ po,
                                                                const float* __restrict__ pml,
                                                                uint16_t* __restrict__ O) {
-  const int pair = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
-  if (pair >= tv.n_rows * ASV_Q_HEADS) return;
+  constexpr int kGroups = ASV_Q_HEADS / kHeadsPerWave;
+  const int item = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+  if (item >= tv.n_rows * kGroups) return;
   const int lane = threadIdx.x & 63;
-  const int r = pair / ASV_Q_HEADS;
-  const int h = pair - r * ASV_Q_HEADS;
+  const int r = item / kGroups;
+  const int h = (item - r * kGroups) * kHeadsPerWave + (lane >> 4);
+  const int c = lane & 15;
   const asv_row row = uniform(cload(tv.rows + r));
   const asv_seg S = uniform(cload(tv.segs + row.stream));
   const int nt = splits_before(S, row.nkeys);
@@ -49,51 +58,46 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_rows(TableView tv,
   const float2* ml = reinterpret_cast<const float2*>(pml);
   const float ninf = -__builtin_inff();
 
-  // (m, l) of split t0 + lane; most rows have at most 64 splits, so the
-  // first chunk's values are kept for the second pass
-  float2 v0 = make_float2(ninf, 0.f);
-  if (lane < nt) v0 = gload(ml + rec0 + lane * step);
-  float M = (v0.y != 0.f) ? v0.x : ninf;
-  for (int t = 64 + lane; t < nt; t += 64) {
+  float M = ninf;
+  for (int t = c; t < nt; t += 16) {
     const float2 v = gload(ml + rec0 + t * step);
     if (v.y != 0.f) M = fmaxf(M, v.x);
   }
-  M = wave_max(M);
+  M = row16_max(M);
 
-  float L = 0.f, acc = 0.f;
-  const float* o = po + rec0 * ASV_HEAD_DIM + lane;
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const float* o = po + rec0 * ASV_HEAD_DIM + 4 * c;
   const int64_t ostep = step * ASV_HEAD_DIM;
-  for (int t0 = 0; t0 < nt; t0 += 64) {
-    const float2 v = (t0 == 0) ? v0 : ((t0 + lane < nt) ? gload(ml + rec0 + (t0 + lane) * step)
-                                                          : make_float2(ninf, 0.f));
+  auto add = [&](const float2 v, const f32x4 ot) {
     const float w = exp2_((v.x - M) * kLog2e) * v.y;
-    const uint64_t empty = __ballot(v.y == 0.f);
-    const int n = min(64, nt - t0);
-    int j0 = 0;
-    for (; j0 + 8 <= n; j0 += 8) {
-      // eight splits at a time, their loads in flight together
-      float ot[8];
+    const bool use = v.y != 0.f;
+    L = use ? L + w : L;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) ot[k] = gload(o + (t0 + j0 + k) * ostep);
+    for (int e = 0; e < 4; ++e) acc[e] = use ? __builtin_fmaf(w, ot[e], acc[e]) : acc[e];
+  };
+  int t = 0;
+  for (; t + 8 <= nt; t += 8) {
+    // eight splits at a time, their loads in flight together
+    float2 v[8];
+    f32x4 ot[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = j0 + k;
-        const bool use = !((empty >> j) & 1u);
-        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
-        L = use ? L + wj : L;
-        acc = use ? __builtin_fmaf(wj, ot[k], acc) : acc;
-      }
+    for (int k = 0; k < 8; ++k) {
+      v[k] = gload(ml + rec0 + (t + k) * step);
+      ot[k] = gload(reinterpret_cast<const f32x4*>(o + (t + k) * ostep));
     }
-    for (int j = j0; j < n; ++j) {  // the rest, one split at a time
-      const float ot = gload(o + (t0 + j) * ostep);
-      const bool use = !((empty >> j) & 1u);
-      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
-      L = use ? L + wj : L;
-      acc = use ? __builtin_fmaf(wj, ot, acc) : acc;
-    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) add(v[k], ot[k]);
   }
-  const float y = (L != 0.f) ? acc / L : 0.f;
-  gstore(O + (int64_t(r) * ASV_Q_HEADS + h) * ASV_HEAD_DIM + lane, uint16_t(f32_to_bf16(y)));
+  for (; t < nt; ++t)  // the rest, one split at a time
+    add(gload(ml + rec0 + t * step), gload(reinterpret_cast<const f32x4*>(o + t * ostep)));
+  uint32_t y[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = f32_to_bf16((L != 0.f) ? acc[e] / L : 0.f);
+  gstore(reinterpret_cast<unsigned long long*>(O + (int64_t(r) * ASV_Q_HEADS + h) * ASV_HEAD_DIM +
+                                               4 * c),
+         (unsigned long long)(y[0] | (y[1] << 16)) |
+             ((unsigned long long)(y[2] | (y[3] << 16)) << 32));
 }
 
 }  // namespace
@@ -108,8 +112,8 @@ extern "C" int asv_attn_merge(const asv_table_info* info, const void* dev_blob,
   const asv::TableView tv = asv::make_view(*info, dev_blob);
   const float* po = partials;
   const float* pml = partials + info->partial_count * ASV_HEAD_DIM;
-  const unsigned pairs = unsigned(info->n_rows) * ASV_Q_HEADS;
-  hipLaunchKernelGGL(asv::merge_rows, dim3((pairs + asv::kMergeWaves - 1) / asv::kMergeWaves),
+  const unsigned items = unsigned(info->n_rows) * (ASV_Q_HEADS / asv::kHeadsPerWave);
+  hipLaunchKernelGGL(asv::merge_rows, dim3((items + asv::kMergeWaves - 1) / asv::kMergeWaves),
                      dim3(64 * asv::kMergeWaves), 0,
                      static_cast<hipStream_t>(stream), tv, po, pml, o);
   return hipGetLastError() == hipSuccess ? ASV_OK : ASV_E_HIP;
