@@ -207,15 +207,15 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 }
 
 // Rebase q tile u (wave-uniform, rare): every column moves its base up to
-// its max score so far (smax: the lane's max of this sub-block); x * 1.0f
-// leaves the bits of columns that do not move unchanged. PSHIFT: weights
+// its max score so far (ms: the lane's max of every score it has seen);
+// x * 1.0f leaves the bits of columns that do not move unchanged. PSHIFT: weights
 // are taken 2^PSHIFT times their value at the base (l and o alike, so o is
 // unchanged and l is divided back at the end).
 template <int QPW, int PSHIFT = 0>
-__device__ __forceinline__ void rebase(WaveState<QPW>& st, int u, float smax) {
+__device__ __forceinline__ void rebase(WaveState<QPW>& st, int u, float ms) {
   const float c = kScale * kLog2e;
   const float ninf = -__builtin_inff();
-  const float mx = max_xor32(max_xor16(smax));
+  const float mx = max_xor32(max_xor16(ms));
   const float mn = fmaxf(st.mref[u], mx);
   const float alpha = (mn > st.mref[u]) ? exp2_((st.mref[u] - mn) * c) : 1.f;
   st.mref[u] = mn;
@@ -541,21 +541,22 @@ __device__ __forceinline__ void sub_block(const char* sub, int kb, int keys, boo
     k[3] = rd(kr1 + 512);
   }
   float sc[QPW][8];
-  float smax[QPW];
   bool over = false;
 #pragma unroll
   for (int u = 0; u < QPW; ++u) {
     scores<QPW, EDGE>(k, qop, u, kb, G, nq, sc[u]);
-    smax[u] = max3(max3(sc[u][0], sc[u][1], sc[u][2]), max3(sc[u][3], sc[u][4], sc[u][5]),
-                   __builtin_elementwise_maximum(sc[u][6], sc[u][7]));
-    st.ms[u] = __builtin_elementwise_maximum(st.ms[u], smax[u]);
-    over |= smax[u] > st.thr[u];
+    // the running max takes the sub-block's scores in four v_maximum3; the
+    // threshold test reads it (scores seen before this sub-block are below
+    // the threshold already: a rebase puts it above every score so far)
+    st.ms[u] = max3(st.ms[u], max3(sc[u][0], sc[u][1], sc[u][2]), max3(sc[u][3], sc[u][4], sc[u][5]));
+    st.ms[u] = max3(st.ms[u], sc[u][6], sc[u][7]);
+    over |= st.ms[u] > st.thr[u];
   }
   bool rescale = false;
   if constexpr (VMODE == kVGroupF16) rescale = vword != st.ev;
   if (first || rescale || __any(over)) {
 #pragma unroll
-    for (int u = 0; u < QPW; ++u) rebase<QPW, (VMODE == kVGroupF16) ? kPShift16 : 0>(st, u, smax[u]);
+    for (int u = 0; u < QPW; ++u) rebase<QPW, (VMODE == kVGroupF16) ? kPShift16 : 0>(st, u, st.ms[u]);
     if constexpr (VMODE == kVGroupF16) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
