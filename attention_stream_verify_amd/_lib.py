@@ -15,7 +15,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libasv.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 HIDDEN = 2048
 CONV_IN = 6144
 Q_HEADS = 32
@@ -80,8 +80,8 @@ SEG_DTYPE = np.dtype([("row0", "<i4"), ("rows", "<i4"), ("keys", "<i4"), ("cap",
                       ("split_tail", "<i4"), ("nbig", "<i4"), ("reserved", "<i4", (2,))])
 ROW_DTYPE = np.dtype([("stream", "<i4"), ("pos", "<i4"), ("nkeys", "<i4"), ("tile", "<i4")])
 TILE_DTYPE = np.dtype([("stream", "<i4"), ("row0", "<i4"), ("nrows", "<i4"), ("pos0", "<i4")])
-WORK_DTYPE = np.dtype([("tile", "<i4"), ("head", "<i2"), ("ntiles", "<i2"), ("split", "<i4"),
-                       ("keys", "<i4")])
+WORK_DTYPE = np.dtype([("tile", "<i4"), ("head", "i1"), ("ntiles", "i1"), ("stream", "<i2"),
+                       ("split", "<i4"), ("keys", "<i4")])
 
 _lib = None
 

@@ -672,31 +672,41 @@ __device__ __forceinline__ TileState get_tile(const float* slot, int lane) {
   return t;
 }
 
+// What every item reads first: its work record, then, in one round trip
+// (all four depend on the work record only), its first tile, its stream's
+// record and the stream's K and V addresses for the layer.
+struct Item {
+  asv_work wk;
+  asv_tile T;
+  asv_seg S;
+  const uint16_t* K;
+  const uint16_t* V;
+};
+
 // A block of 4 waves runs one work item; every wave holds all QPW q tiles
 // of the tile (QPW = ceil(rows/4)) and its own stripe of the split's keys;
 // at the end the waves fold their states through LDS in wave order.
 template <int QPW, int AUX>
-__device__ __forceinline__ void attn_item(const TableView& tv, int layer,
+__device__ __forceinline__ void attn_item(const TableView& tv, const Item& it,
                                           const uint16_t* __restrict__ Q, float* __restrict__ po,
-                                          float* __restrict__ pml, const asv_work wk,
-                                          char* __restrict__ ringA, char* __restrict__ ringB) {
+                                          float* __restrict__ pml, char* __restrict__ ringA,
+                                          char* __restrict__ ringB) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = lane >> 4;
   const int c16 = lane & 15;
-  const asv_tile T = uniform(cload(tv.tiles + wk.tile));
-  const asv_seg S = uniform(cload(tv.segs + T.stream));
+  const asv_work& wk = it.wk;
+  const asv_tile& T = it.T;
+  const asv_seg& S = it.S;
   const int g = wk.head;
   // visible key counts come from the table's rows (causal: the tile's first
   // row sees the fewest; block tables: every row sees all keys)
   const int n_first = uni(cload(tv.rows + T.row0).nkeys);
-  const int n_last = uni(cload(tv.rows + T.row0 + T.nrows - 1).nkeys);
   const int k0 = split_start(S, wk.split);
-  const int k1 = min(split_start(S, wk.split + 1), n_last);
+  const int k1 = k0 + wk.keys;  // the split's keys the tile's last row sees
   const int64_t head_elems = int64_t(S.cap) * ASV_HEAD_DIM;
-  const int64_t sel = int64_t(layer) * tv.n_streams + T.stream;
-  const uint16_t* Kh = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.kp + sel))) + g * head_elems;
-  const uint16_t* Vh = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.vp + sel))) + g * head_elems;
+  const uint16_t* Kh = it.K + g * head_elems;
+  const uint16_t* Vh = it.V + g * head_elems;
 
   // per-lane byte offsets: HBM chunks fetched into K group j and V group dt
   // (1 KB on per dt), and the K operands read back for d-steps 0 and 1
@@ -869,31 +879,28 @@ __device__ __forceinline__ void issue_quarter(char* slot, const uint16_t* __rest
 }
 
 template <int AUX>
-__device__ __forceinline__ void attn_group(const TableView& tv, int layer,
+__device__ __forceinline__ void attn_group(const TableView& tv, const Item& it,
                                            const uint16_t* __restrict__ Q, float* __restrict__ po,
-                                           float* __restrict__ pml, const asv_work wk,
-                                           char* __restrict__ ringA, char* __restrict__ ringB,
-                                           uint32_t* __restrict__ vword) {
+                                           float* __restrict__ pml, char* __restrict__ ringA,
+                                           char* __restrict__ ringB, uint32_t* __restrict__ vword) {
   constexpr int QPW = 4;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = lane >> 4;
   const int c16 = lane & 15;
+  const asv_work& wk = it.wk;
   const bool active = wave < wk.ntiles;
-  const asv_tile T0 = uniform(cload(tv.tiles + wk.tile));
-  const asv_tile TL = uniform(cload(tv.tiles + wk.tile + wk.ntiles - 1));
+  const asv_tile& T0 = it.T;
   const asv_tile T = uniform(cload(tv.tiles + wk.tile + (active ? wave : 0)));
-  const asv_seg S = uniform(cload(tv.segs + T0.stream));
+  const asv_seg& S = it.S;
   const int g = wk.head;
-  // the group's first row sees the fewest keys, its last row the most
+  // the group's first row sees the fewest keys
   const int n_first = uni(cload(tv.rows + T0.row0).nkeys);
-  const int n_last = uni(cload(tv.rows + TL.row0 + TL.nrows - 1).nkeys);
   const int k0 = split_start(S, wk.split);
-  const int k1 = min(split_start(S, wk.split + 1), n_last);
+  const int k1 = k0 + wk.keys;  // the split's keys the group's last row sees
   const int64_t head_elems = int64_t(S.cap) * ASV_HEAD_DIM;
-  const int64_t sel = int64_t(layer) * tv.n_streams + T0.stream;
-  const uint16_t* Kh = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.kp + sel))) + g * head_elems;
-  const uint16_t* Vh = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.vp + sel))) + g * head_elems;
+  const uint16_t* Kh = it.K + g * head_elems;
+  const uint16_t* Vh = it.V + g * head_elems;
 
   // this wave's quarter of each sub-block: K group `wave`, V group `wave`
   const uint32_t koff = uint32_t(wave * 1024) + k_fetch(lane, wave);
@@ -1032,40 +1039,49 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split(TableView tv, int laye
   __shared__ __attribute__((aligned(16))) char ringA[kWaves * kSubBytes];
   __shared__ __attribute__((aligned(16))) char ringB[kWaves * kSubBytes];
   __shared__ uint32_t vword[kGroupSlots];  // group items: V exponents a slot
-  const asv_work wk = uniform(cload(tv.work + blockIdx.x));
-  const asv_tile T = uniform(cload(tv.tiles + wk.tile));
+  Item it;
+  it.wk = uniform(cload(tv.work + blockIdx.x));
+  const asv_work& wk = it.wk;
+  it.T = uniform(cload(tv.tiles + wk.tile));
+  it.S = uniform(cload(tv.segs + wk.stream));
+  const int64_t sel = int64_t(layer) * tv.n_streams + wk.stream;
+  it.K = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.kp + sel)));
+  it.V = reinterpret_cast<const uint16_t*>(uniform_ptr(cload(tv.vp + sel)));
+  // no instruction moves across this point, so the four reads above are all
+  // issued before the first wait for any of them
+  __builtin_amdgcn_sched_barrier(0);
+  const asv_tile& T = it.T;
   const int nqt = (T.nrows + 3) >> 2;
   // an item that covers every tile of its stream reads its K/V once: stream
   // it past the caches; items of a longer stream re-read the same keys
-  const bool once =
-      T.pos0 == 0 && uni(cload(tv.segs + T.stream).rows) <= ASV_TILE_ROWS * int(wk.ntiles);
+  const bool once = T.pos0 == 0 && it.S.rows <= ASV_TILE_ROWS * int(wk.ntiles);
   if constexpr (QPW_MAX >= 4) {
     // groups come only from streams of more than one tile, whose tiles
     // (the last aside) hold 16 rows, so a round that has them launches this
     // instance
     if (wk.ntiles > 1) {
-      if (once) return attn_group<kStream>(tv, layer, Q, po, pml, wk, ringA, ringB, vword);
-      return attn_group<0>(tv, layer, Q, po, pml, wk, ringA, ringB, vword);
+      if (once) return attn_group<kStream>(tv, it, Q, po, pml, ringA, ringB, vword);
+      return attn_group<0>(tv, it, Q, po, pml, ringA, ringB, vword);
     }
     if (nqt == 4) {
-      if (once) return attn_item<4, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB);
-      return attn_item<4, 0>(tv, layer, Q, po, pml, wk, ringA, ringB);
+      if (once) return attn_item<4, kStream>(tv, it, Q, po, pml, ringA, ringB);
+      return attn_item<4, 0>(tv, it, Q, po, pml, ringA, ringB);
     }
   }
   if constexpr (QPW_MAX >= 3) {
     if (nqt == 3) {
-      if (once) return attn_item<3, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB);
-      return attn_item<3, 0>(tv, layer, Q, po, pml, wk, ringA, ringB);
+      if (once) return attn_item<3, kStream>(tv, it, Q, po, pml, ringA, ringB);
+      return attn_item<3, 0>(tv, it, Q, po, pml, ringA, ringB);
     }
   }
   if constexpr (QPW_MAX >= 2) {
     if (nqt == 2) {
-      if (once) return attn_item<2, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB);
-      return attn_item<2, 0>(tv, layer, Q, po, pml, wk, ringA, ringB);
+      if (once) return attn_item<2, kStream>(tv, it, Q, po, pml, ringA, ringB);
+      return attn_item<2, 0>(tv, it, Q, po, pml, ringA, ringB);
     }
   }
-  if (once) return attn_item<1, kStream>(tv, layer, Q, po, pml, wk, ringA, ringB);
-  attn_item<1, 0>(tv, layer, Q, po, pml, wk, ringA, ringB);
+  if (once) return attn_item<1, kStream>(tv, it, Q, po, pml, ringA, ringB);
+  attn_item<1, 0>(tv, it, Q, po, pml, ringA, ringB);
 }
 
 }  // namespace

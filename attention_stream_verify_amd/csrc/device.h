@@ -115,8 +115,8 @@ __device__ __forceinline__ asv_tile uniform(asv_tile r) {
   return asv_tile{uni(r.stream), uni(r.row0), uni(r.nrows), uni(r.pos0)};
 }
 __device__ __forceinline__ asv_work uniform(asv_work r) {
-  return asv_work{uni(r.tile), int16_t(uni(r.head)), int16_t(uni(r.ntiles)), uni(r.split),
-                  uni(r.keys)};
+  return asv_work{uni(r.tile), int8_t(uni(r.head)), int8_t(uni(r.ntiles)), int16_t(uni(r.stream)),
+                  uni(r.split), uni(r.keys)};
 }
 __device__ __forceinline__ asv_row uniform(asv_row r) {
   return asv_row{uni(r.stream), uni(r.pos), uni(r.nkeys), uni(r.tile)};

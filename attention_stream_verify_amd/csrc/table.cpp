@@ -71,6 +71,8 @@ int32_t split_start(const Plan& p, int32_t t) {
 
 static_assert(sizeof(asv_seg) == 48, "asv_seg layout");
 static_assert(sizeof(asv_work) == 16, "asv_work layout");
+// every stream holds a row, so a stream index fits asv_work's int16 field
+static_assert(ASV_MAX_ROWS <= 32767, "asv_work stream field");
 
 // Tiles of one group item (one a wave of the attention block).
 constexpr int32_t kGroupTiles = 4;
@@ -216,7 +218,7 @@ int build_table(const asv_stream_desc* streams, int32_t n_streams, const void* c
       const int32_t k0 = split_start(pl, sp);
       const int32_t k1 = std::min(sp + 1 < g.nsplit ? split_start(pl, sp + 1) : g.keys, n_last);
       for (int32_t h = 0; h < ASV_KV_HEADS; ++h)
-        work.push_back({ti, int16_t(h), int16_t(nt), sp, k1 - k0});
+        work.push_back({ti, int8_t(h), int8_t(nt), int16_t(t.stream), sp, k1 - k0});
     }
     ti += nt;
   }

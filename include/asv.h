@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define ASV_ABI_VERSION 3
+#define ASV_ABI_VERSION 4
 
 /* Model dimensions compiled into the kernels (LFM2.5-24B-A2B shapes). */
 #define ASV_HIDDEN 2048          /* conv channels, attention row width      */
@@ -118,12 +118,15 @@ typedef struct {      /* runs of <= 16 rows of one stream                  */
 
 typedef struct {      /* one attention work item: (tiles, kv head, split) */
   int32_t tile;       /* its first tile                                   */
-  int16_t head;
-  int16_t ntiles;     /* 1: one tile, its keys striped over the block's
+  int8_t head;
+  int8_t ntiles;      /* 1: one tile, its keys striped over the block's
                          waves; 2-4: that many consecutive tiles of one
                          stream, a wave each, every wave walking all of
                          the split's keys (streams of more than one tile
                          are cut into groups of 4 tiles, the last shorter) */
+  int16_t stream;     /* the tiles' stream (also in the tile records; here
+                         so that a block reads its stream's records and
+                         K/V addresses beside its tile record, not after) */
   int32_t split;
   int32_t keys;       /* keys the item visits: the split's keys that the
                          last row of its last tile sees                   */

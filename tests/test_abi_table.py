@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(asv._lib.LIB_PATH)
     for name in _declared():
         assert hasattr(L, name), name
-    assert asv.abi_version() == 3
+    assert asv.abi_version() == 4
     assert asv.strerror(-4) == "caller buffer too small"
 
 
@@ -88,6 +88,7 @@ def _compare(streams, full=False):
     got = sorted(zip(w["tile"].tolist(), w["head"].tolist(), w["split"].tolist(),
                      w["ntiles"].tolist()))
     assert got == sorted(map(tuple, o.work.tolist()))
+    assert np.array_equal(w["stream"], o.tiles[w["tile"], 0])
     cost = w["keys"].astype(np.int64) * np.where(w["ntiles"] > 1, 4, 1)
     assert all(cost[i] >= cost[i + 1] for i in range(len(w) - 1))
     for ti, sp, nt, k in zip(w["tile"], w["split"], w["ntiles"], w["keys"]):
