@@ -364,6 +364,11 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
   return uint32_t(__builtin_amdgcn_readfirstlane(int(x)));
 }
 
+// A wave's V exponent for its d tile, and the lowest it has taken in the item.
+struct VScale {
+  int e = 142, emin = 142;
+};
+
 // Wave w's pass over its own quarter of a landed sub-block (d tile w of V,
 // all 32 keys: the 16 bytes each lane loaded itself), before the block
 // barrier. V past the key count is zeroed; the quarter is then scaled by 2^e
@@ -388,11 +393,6 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
 //
 // convert_quarter takes the 16 bytes already read from LDS address a, where
 // it writes them back.
-// A wave's V exponent for its d tile, and the lowest it has taken in the item.
-struct VScale {
-  int e = 142, emin = 142;
-};
-
 __device__ __forceinline__ void convert_quarter(u32x4 x, uint32_t a, uint32_t word_addr, int wave,
                                                 int lane, int kb, int keys, VScale& vs) {
   if (kb + 32 > keys) {
