@@ -251,6 +251,7 @@ def _edge_rows(t):
     [(64, 100, 128), (100, 150, 160)],           # groups of 4 and 3 tiles, fewer sub-blocks than ring slots
     [(96, 9000, 9024)],                          # 6 tiles: a group of 4, then one of 2
     [(80, 5000, 5024), (1, 40, 64)],             # 5 tiles: a group of 4, then a lone tile
+    [(17, 17, 32), (31, 31, 32), (20, 40, 64)],  # groups of one or two sub-blocks, a one-row last tile
 ])
 def test_attention_edge_shapes(streams):
     rnd = workloads.Round(0, "cuda", n_conv=0, n_attn=1, streams=streams, with_logits=False)
@@ -368,6 +369,7 @@ def test_block_attention_parity(config):
     [(16, 14337, 14368), (24, 21505, 21536)],    # 3 and 4 splits, the last one short
     [(64, 100, 128), (100, 150, 160)],           # groups of 4 and 3 tiles, fewer sub-blocks than ring slots
     [(96, 9000, 9024)],                          # 6 tiles: a group of 4, then one of 2
+    [(17, 17, 32), (31, 31, 32), (20, 40, 64)],  # groups of one or two sub-blocks, a one-row last tile
 ])
 def test_block_attention_edge_shapes(streams):
     rnd = workloads.Round(0, "cuda", n_conv=0, n_attn=1, streams=streams, with_logits=False)
