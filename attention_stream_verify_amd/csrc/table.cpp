@@ -27,7 +27,9 @@ namespace {
 // 1,024, 1,280, 1,792 or 2,048 did); 16-row tiles take splits of about 7,168
 // keys, which at 131,072-key contexts puts one tile's 8 heads x 19 splits,
 // and four such streams' 496 work items, on the 512 blocks the device holds
-// at once.
+// at once. Prompt chunks (streams of more than one tile) take at most 5,120
+// keys a split: their group items are arithmetic-bound, and shorter ones
+// end closer together.
 //
 // Windows of up to 8 rows cut their keys into n equal splits. 16-row tiles
 // take two sizes, the first ceil(n / 2) splits 5/4 the size of the rest:
@@ -37,6 +39,7 @@ namespace {
 // larger share; the two then finish together instead of the second block
 // running alone at the end.
 int32_t split_cap(int32_t rows) {
+  if (rows > ASV_TILE_ROWS) return 5120;  // prompt chunks
   const int32_t wt = rows < ASV_TILE_ROWS ? rows : ASV_TILE_ROWS;
   if (wt <= 2) return 768;
   if (wt <= 4) return 1024;
@@ -76,6 +79,8 @@ static_assert(ASV_MAX_ROWS <= 32767, "asv_work stream field");
 
 // Tiles of one group item (one a wave of the attention block).
 constexpr int32_t kGroupTiles = 4;
+// Work-list runs: 256 blocks, one a CU of the device, dispatched first.
+constexpr size_t kRun = 256;
 
 int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
 
@@ -203,7 +208,10 @@ int build_table(const asv_stream_desc* streams, int32_t n_streams, const void* c
   // key the last row of the item's last tile sees. A stream of one tile is
   // one item a split and head; a longer stream (a prompt chunk) is cut into
   // groups of up to kGroupTiles consecutive tiles, which read each key once
-  // for the whole group. Costliest first, so long items start early.
+  // for the whole group. Each kind costliest first, so long items start
+  // early; the two kinds in alternating runs of 256 (kRun), so that the
+  // first blocks the device places, one a CU and then a second on each
+  // CU, pair an arithmetic-bound group with an HBM-bound one-tile item.
   std::vector<asv_work> work;
   for (int32_t ti = 0; ti < static_cast<int32_t>(tiles.size());) {
     const asv_tile& t = tiles[ti];
@@ -225,6 +233,16 @@ int build_table(const asv_stream_desc* streams, int32_t n_streams, const void* c
   auto cost = [](const asv_work& w) { return int64_t(w.keys) * (w.ntiles > 1 ? 4 : 1); };
   std::stable_sort(work.begin(), work.end(),
                    [&](const asv_work& a, const asv_work& b) { return cost(a) > cost(b); });
+  {
+    std::vector<asv_work> grp, one;
+    for (const asv_work& x : work) (x.ntiles > 1 ? grp : one).push_back(x);
+    work.clear();
+    size_t i = 0, j = 0;
+    while (i < grp.size() || j < one.size()) {
+      for (size_t k = 0; k < kRun && i < grp.size(); ++k) work.push_back(grp[i++]);
+      for (size_t k = 0; k < kRun && j < one.size(); ++k) work.push_back(one[j++]);
+    }
+  }
 
   // ---- blob layout
   asv_table_info in;

@@ -131,8 +131,9 @@ typedef struct {      /* one attention work item: (tiles, kv head, split) */
   int32_t keys;       /* keys the item visits: the split's keys that the
                          last row of its last tile sees                   */
 } asv_work;
-/* The work list is ordered by cost, largest first: keys for one-tile
- * items, 4 x keys for groups (each wave walks every key). */
+/* The work list holds each kind of item by cost, largest first (keys for
+ * one-tile items, 4 x keys for groups, whose waves each walk every key), the
+ * two kinds in alternating runs of 256 items, groups first. */
 
 /* What asv_seg_table_build reports (host). Offsets are byte offsets of the
  * arrays inside the blob; the same struct is passed back to every call. */
@@ -150,7 +151,7 @@ typedef struct {
   int64_t off_segs;        /* asv_seg[n_streams]                              */
   int64_t off_rows;        /* asv_row[n_rows]                                 */
   int64_t off_tiles;       /* asv_tile[n_tiles]                               */
-  int64_t off_work;        /* asv_work[n_work], costliest first               */
+  int64_t off_work;        /* asv_work[n_work], in the order described above  */
   int64_t off_conv_state;  /* uint64 device addresses [n_conv_layers][n_streams] */
   int64_t off_k;           /* uint64 device addresses [n_attn_layers][n_streams] */
   int64_t off_v;           /* uint64 device addresses [n_attn_layers][n_streams] */

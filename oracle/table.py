@@ -18,7 +18,8 @@ definitions (the readings are listed in the design notes):
 * split plan: the splits depend only on the stream's own rows and keys (so
   a shared round gives the same bits as each stream alone): with
   wt = min(w_s, 16), the cap C_s = 768 (wt <= 2), 1024 (wt <= 4),
-  1536 (wt <= 8), 7168 (otherwise), the keys are cut into
+  1536 (wt <= 8), 7168 (otherwise), and 5120 for a stream of more than 16
+  rows (a prompt chunk), the keys are cut into
   n_s = ceil(K_s / C_s) consecutive splits, each starting at a multiple of
   32 keys, the last one ending at K_s:
   - equal splits (wt <= 8, or n_s = 1): size S_s = ceil(K_s / n_s) rounded
@@ -61,6 +62,8 @@ MAX_KEYS = 131072
 
 def split_cap(rows):
     """Largest split C_s for a stream of ``rows`` window rows."""
+    if int(rows) > TILE_ROWS:
+        return 5120
     wt = min(int(rows), TILE_ROWS)
     if wt <= 2:
         return 768

@@ -89,8 +89,23 @@ def _compare(streams, full=False):
                      w["ntiles"].tolist()))
     assert got == sorted(map(tuple, o.work.tolist()))
     assert np.array_equal(w["stream"], o.tiles[w["tile"], 0])
+    # each kind costliest first, the kinds in alternating runs of 256 (groups
+    # first) until one runs out
     cost = w["keys"].astype(np.int64) * np.where(w["ntiles"] > 1, 4, 1)
-    assert all(cost[i] >= cost[i + 1] for i in range(len(w) - 1))
+    grp = w["ntiles"] > 1
+    for kind in (grp, ~grp):
+        c = cost[kind]
+        assert all(c[i] >= c[i + 1] for i in range(len(c) - 1))
+    ng, n1 = int(grp.sum()), int((~grp).sum())
+    expect, i, j = [], 0, 0
+    while i < ng or j < n1:
+        take = min(256, ng - i)
+        expect += [True] * take
+        i += take
+        take = min(256, n1 - j)
+        expect += [False] * take
+        j += take
+    assert grp.tolist() == expect
     for ti, sp, nt, k in zip(w["tile"], w["split"], w["ntiles"], w["keys"]):
         s, _r0, n, p0 = o.tiles[ti + nt - 1]
         last = o.keys[s] if full else o.keys[s] - o.rows[s] + p0 + n

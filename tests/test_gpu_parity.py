@@ -245,8 +245,8 @@ def _edge_rows(t):
     [(33, 600, 640), (1, 5000, 5024)],           # a 3-tile chunk
     [(512, 3000, 3072)],                         # a prompt chunk of 32 tiles
     [(16, 7169, 7200)],                          # two split sizes: 4,000 then 3,169 keys
-    [(17, 20000, 20000)],                        # 7,168 x 2 then 5,664; a one-row second tile
-    [(16, 14337, 14368), (24, 21505, 21536)],    # 3 and 4 splits, the last one short
+    [(17, 20000, 20000)],                        # 5,568 x 2 then 4,448 x 2; a one-row second tile
+    [(16, 14337, 14368), (24, 21505, 21536)],    # 3 and 5 splits, the last one short
     [(2048, 131072, 131072)],                    # both maxima: 2,048 rows, 131,072 keys
     [(64, 100, 128), (100, 150, 160)],           # groups of 4 and 3 tiles, fewer sub-blocks than ring slots
     [(96, 9000, 9024)],                          # 6 tiles: a group of 4, then one of 2
@@ -365,8 +365,8 @@ def test_block_attention_parity(config):
     [(33, 600, 640), (1, 5000, 5024)],           # a 3-tile chunk
     [(512, 3000, 3072)],                         # a prompt chunk of 32 tiles
     [(16, 7169, 7200)],                          # two split sizes: 4,000 then 3,169 keys
-    [(17, 20000, 20000)],                        # 7,168 x 2 then 5,664; a one-row second tile
-    [(16, 14337, 14368), (24, 21505, 21536)],    # 3 and 4 splits, the last one short
+    [(17, 20000, 20000)],                        # 5,568 x 2 then 4,448 x 2; a one-row second tile
+    [(16, 14337, 14368), (24, 21505, 21536)],    # 3 and 5 splits, the last one short
     [(64, 100, 128), (100, 150, 160)],           # groups of 4 and 3 tiles, fewer sub-blocks than ring slots
     [(96, 9000, 9024)],                          # 6 tiles: a group of 4, then one of 2
     [(17, 17, 32), (31, 31, 32), (20, 40, 64)],  # groups of one or two sub-blocks, a one-row last tile

@@ -124,7 +124,7 @@ def test_table_invariants_random(streams):
 def test_table_split_plan_by_window():
     # the cap depends only on the stream's own rows
     assert [table.split_cap(w) for w in (1, 2, 3, 4, 5, 8, 9, 16, 17, 512)] == \
-        [768, 768, 1024, 1024, 1536, 1536, 7168, 7168, 7168, 7168]
+        [768, 768, 1024, 1024, 1536, 1536, 7168, 7168, 5120, 5120]
     # windows of up to 8 rows, equal splits by hand: 1,000 / 2 = 500 -> 512;
     # 100 / 1 -> 128; 4,096 / ceil(4,096 / 768) = 4,096 / 6 = 682.7 -> 704;
     # 32,768 / ceil(32,768 / 1,536) = 32,768 / 22 = 1,489.5 -> 1,504 (cap 1,536)
@@ -145,7 +145,11 @@ def test_table_split_plan_by_window():
          (7008, 7008, 1, 1)]
     assert table.split_bounds(16, 65536).tolist() == \
         [0, 7296, 14592, 21888, 29184, 36480, 42304, 48128, 53952, 59776, 65536]
-    assert table.split_bounds(17, 131072)[-2:].tolist() == [125120, 131072]
+    # prompt chunks (more than 16 rows) take the 5,120 cap, two sizes by hand:
+    #  131,072: n = 26, b = 13: A = ceil(655,360 / 117) = 5,602 -> 5,632,
+    #           B = ceil(57,856 / 13) = 4,451 -> 4,480; last split [126,976, 131,072)
+    assert table.split_plan(17, 131072) == (5632, 4480, 13, 26)
+    assert table.split_bounds(17, 131072)[-2:].tolist() == [126976, 131072]
 
 
 @settings(max_examples=300, deadline=None)
