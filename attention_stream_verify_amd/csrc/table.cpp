@@ -22,9 +22,9 @@ namespace {
 // consecutive splits, each starting at a multiple of 32 keys. Few short
 // windows make many small splits (one- and two-row windows: at most 768
 // keys, which puts a 16-stream decode round with 512-4,096 keys in one
-// round of the device's 512 resident blocks; windows of 5 to 8 rows: at most 1,536
-// keys, which evens out the 16 x 8-row verify round's items better than
-// 1,024, 1,280, 1,792 or 2,048 did); 16-row tiles take splits of about 7,168
+// round of the device's 512 resident blocks; windows of 5 to 8 rows: at most 2,560
+// keys, which puts the 16 x 8-row verify round's 472 items in one round too,
+// where 1,024-2,304 and 3,072 were slower); 16-row tiles take splits of about 7,168
 // keys, which at 131,072-key contexts puts one tile's 8 heads x 19 splits,
 // and four such streams' 496 work items, on the 512 blocks the device holds
 // at once. Prompt chunks (streams of more than one tile) take at most 5,120
@@ -43,7 +43,7 @@ int32_t split_cap(int32_t rows) {
   const int32_t wt = rows < ASV_TILE_ROWS ? rows : ASV_TILE_ROWS;
   if (wt <= 2) return 768;
   if (wt <= 4) return 1024;
-  if (wt <= 8) return 1536;
+  if (wt <= 8) return 2560;
   return 7168;
 }
 

@@ -85,8 +85,9 @@ typedef struct {      /* one per stream, caller order                     */
   int32_t keys;
   int32_t cap;
   int32_t split_keys; /* A: keys in each of the first nbig splits        */
-  int32_t nsplit;     /* n = ceil(keys / C), C = 768, 1024, 1536 or 7168
-                         by the stream's rows (<= 2, <= 4, <= 8, more)    */
+  int32_t nsplit;     /* n = ceil(keys / C), C = 768, 1024, 2560, 7168 or
+                         5120 by the stream's rows (<= 2, <= 4, <= 8, <= 16,
+                         more)                                            */
   int64_t poff;       /* first partial record of the stream               */
   int32_t split_tail; /* B: keys in each later split (the last one ends
                          at keys)                                         */

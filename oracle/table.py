@@ -18,7 +18,7 @@ definitions (the readings are listed in the design notes):
 * split plan: the splits depend only on the stream's own rows and keys (so
   a shared round gives the same bits as each stream alone): with
   wt = min(w_s, 16), the cap C_s = 768 (wt <= 2), 1024 (wt <= 4),
-  1536 (wt <= 8), 7168 (otherwise), and 5120 for a stream of more than 16
+  2560 (wt <= 8), 7168 (otherwise), and 5120 for a stream of more than 16
   rows (a prompt chunk), the keys are cut into
   n_s = ceil(K_s / C_s) consecutive splits, each starting at a multiple of
   32 keys, the last one ending at K_s:
@@ -70,7 +70,7 @@ def split_cap(rows):
     if wt <= 4:
         return 1024
     if wt <= 8:
-        return 1536
+        return 2560
     return 7168
 
 

@@ -124,12 +124,12 @@ def test_table_invariants_random(streams):
 def test_table_split_plan_by_window():
     # the cap depends only on the stream's own rows
     assert [table.split_cap(w) for w in (1, 2, 3, 4, 5, 8, 9, 16, 17, 512)] == \
-        [768, 768, 1024, 1024, 1536, 1536, 7168, 7168, 5120, 5120]
+        [768, 768, 1024, 1024, 2560, 2560, 7168, 7168, 5120, 5120]
     # windows of up to 8 rows, equal splits by hand: 1,000 / 2 = 500 -> 512;
     # 100 / 1 -> 128; 4,096 / ceil(4,096 / 768) = 4,096 / 6 = 682.7 -> 704;
-    # 32,768 / ceil(32,768 / 1,536) = 32,768 / 22 = 1,489.5 -> 1,504 (cap 1,536)
+    # 32,768 / ceil(32,768 / 2,560) = 32,768 / 13 = 2,520.6 -> 2,528 (cap 2,560)
     assert [table.split_plan(w, k) for (w, k) in ((1, 1000), (3, 100), (1, 4096), (8, 32768))] == \
-        [(512, 512, 2, 2), (128, 128, 1, 1), (704, 704, 6, 6), (1504, 1504, 22, 22)]
+        [(512, 512, 2, 2), (128, 128, 1, 1), (704, 704, 6, 6), (2528, 2528, 13, 13)]
     # 16-row tiles, two sizes by hand (A = ceil(5K / (5b + 4(n - b))) up to 32,
     # B = ceil((K - bA) / (n - b)) up to 32):
     #   65,536: n = 10, b = 5: A = ceil(327,680 / 45) = 7,282 -> 7,296,
