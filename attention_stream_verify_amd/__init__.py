@@ -18,7 +18,7 @@ from ._lib import (  # noqa: F401
     ABI_VERSION, CONV_IN, HEAD_DIM, HIDDEN, KEY_BLOCK, KV_HEADS, MAX_KEYS, MAX_ROWS,
     PARTIAL_FLOATS, Q_HEADS, QKV_WIDTH, SYMBOLS, TILE_ROWS, AsvError, StreamDesc, TableInfo, abi_version,
     MARKOV_MAX_CHAINS, MARKOV_MAX_DEPTH, MARKOV_MAX_RANK, MarkovChain, attn_merge, draft_ids,
-    lib, markov_pack_w2, markov_pick, markov_workspace, partial_floats, row_argmax, row_argmax_noalloc, row_argmax_workspace, seg_table_build,
+    lib, MARKOV_FORMS, markov_pack_w2, markov_pick, markov_workspace, partial_floats, row_argmax, row_argmax_noalloc, row_argmax_workspace, seg_table_build,
     shared_attn, shared_conv, shared_qk, strerror, table_arrays, table_upload,
 )
 from .runner import RoundBuffers  # noqa: F401

@@ -35,7 +35,7 @@ SYMBOLS = [
     "asv_table_upload",
     "asv_shared_conv", "asv_shared_attn", "asv_attn_merge", "asv_row_argmax_workspace",
     "asv_row_argmax", "asv_row_argmax_noalloc", "asv_draft_ids", "asv_markov_workspace",
-    "asv_markov_pick",
+    "asv_markov_pick", "asv_markov_pick_form",
     "asv_markov_pack_w2", "asv_shared_qk",
 ]
 
@@ -126,6 +126,9 @@ def lib():
         L.asv_markov_pick.restype = ctypes.c_int
         L.asv_markov_pick.argtypes = [vp, i64, i64, ctypes.POINTER(MarkovChain), i32, vp, vp, vp,
                                       i64, i32, vp, vp, vp, sz, vp]
+        L.asv_markov_pick_form.restype = ctypes.c_int
+        L.asv_markov_pick_form.argtypes = [vp, i64, i64, ctypes.POINTER(MarkovChain), i32, vp, vp, vp,
+                                           i64, i32, vp, vp, vp, sz, i32, vp]
         L.asv_shared_qk.restype = ctypes.c_int
         L.asv_shared_qk.argtypes = [ctypes.POINTER(TableInfo), vp, i32, vp, vp, vp, ctypes.c_double,
                                     ctypes.c_double, vp, vp]
@@ -317,17 +320,24 @@ def markov_pack_w2(w2, vocab, rank, w2c, stream=None):
            "asv_markov_pack_w2")
 
 
+MARKOV_FORMS = {"auto": 0, "launches": 1, "resident": 2}
+
+
 def markov_pick(base, rows, row_stride, chains, prev0, w1, w2c, vocab, rank, pick, flag, workspace,
-                stream=None):
+                stream=None, form=None):
     """chains: host list of (row0, depth); the rest device tensors as in
-    include/asv.h. workspace: a device tensor of markov_workspace(vocab) bytes."""
+    include/asv_draft.h. workspace: a device tensor of markov_workspace(vocab)
+    bytes. form: None (asv_markov_pick) or "auto" / "launches" / "resident"
+    (asv_markov_pick_form)."""
     n = len(chains)
     arr = (MarkovChain * max(1, n))(*[MarkovChain(int(r), int(d)) for (r, d) in chains])
     nbytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
-    _check(lib().asv_markov_pick(_addr(base), int(rows), int(row_stride), arr, n, _addr(prev0),
-                                 _addr(w1), _addr(w2c), int(vocab), int(rank), _addr(pick),
-                                 _addr(flag), _addr(workspace), nbytes, _stream(stream)),
-           "asv_markov_pick")
+    args = (_addr(base), int(rows), int(row_stride), arr, n, _addr(prev0), _addr(w1), _addr(w2c), int(vocab),
+            int(rank), _addr(pick), _addr(flag), _addr(workspace), nbytes)
+    if form is None:
+        _check(lib().asv_markov_pick(*args, _stream(stream)), "asv_markov_pick")
+    else:
+        _check(lib().asv_markov_pick_form(*args, MARKOV_FORMS[form], _stream(stream)), "asv_markov_pick_form")
 
 
 def shared_qk(info, dev_blob, layer, qkv, q_gain, k_gain, theta, eps, q_out, stream=None):

@@ -38,6 +38,7 @@
 // chains at a time so that each converted W2 value serves four chains.
 
 #include <array>
+#include <atomic>
 #include <climits>
 #include <utility>
 
@@ -81,10 +82,18 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
   return x;
 }
 
-// A block record: bits 8..23 the order key of the block's largest score and
-// bits 0..7 255 - its lane (so the lower token wins a tie inside the block),
-// both 0 when every score of the block is NaN; bit 31 the nonfinite flag.
-constexpr uint32_t kRecKey = 0x00FFFFFFu;
+// A block record of a block of THREADS threads (LB = log2 THREADS bits of
+// lane): bits LB..LB+15 the order key of the block's largest score and bits
+// 0..LB-1 THREADS - 1 - its thread (so the lower token wins a tie inside the
+// block), both 0 when every score of the block is NaN; bit 31 the nonfinite
+// flag.
+template <int THREADS>
+struct RecBits {
+  static constexpr int kLB = __builtin_ctz(THREADS);
+  static_assert((1 << kLB) == THREADS && kLB + 16 <= 31, "a power of two below 2^15");
+  static constexpr uint32_t kKey = (1u << (kLB + 16)) - 1u;
+  static constexpr uint32_t kLane = THREADS - 1u;
+};
 constexpr uint32_t kRecBad = 0x80000000u;
 
 // Fold one chain's records (nblocks of them) in one wave: the largest order
@@ -96,15 +105,17 @@ struct FoldAcc {
   bool bad;
 };
 
+template <int THREADS>
 __device__ __forceinline__ void fold_use(FoldAcc& a, const uint32_t (&e)[8], int b0, int lane) {
+  using R = RecBits<THREADS>;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const uint32_t key = e[u] & kRecKey;
+    const uint32_t key = e[u] & R::kKey;
     a.bad |= (e[u] & kRecBad) != 0u;
     if (key != 0u) {
       const uint32_t b = uint32_t(b0 + u * 64 + lane);
-      const uint32_t tok = b * kThreads + (kThreads - 1 - (key & 0xFFu));
-      const uint32_t hi = key >> 8, lo = ~tok;
+      const uint32_t tok = b * THREADS + (R::kLane - (key & R::kLane));
+      const uint32_t hi = key >> R::kLB, lo = ~tok;
       if (hi > a.hi || (hi == a.hi && lo > a.lo)) {
         a.hi = hi;
         a.lo = lo;
@@ -135,6 +146,86 @@ __device__ __forceinline__ void fold_finish(FoldAcc a, uint32_t& tok, bool& bad)
   }
   tok = a.hi != 0u ? ~a.lo : 0u;
   bad = __any(a.bad);
+}
+
+// One depth's scores for the thread's token v: chains 0..n-1 of the depth
+// (chain i's logits row row_of(i), its previous token s_prev[i]), four at a
+// time so that each converted W2 value serves four chains. For chain i it
+// leaves the wave's best record (the block-record layout, without the flag)
+// in s_key[wave][i] and the wave's nonfinite-or-invalid flag in
+// s_bad[wave][i]. w holds the token's rank/8 W2 chunks; s_w1[i] chain i's W1
+// row in float32.
+template <int NCH, int THREADS, class RowOf>
+__device__ __forceinline__ void score_depth(int n, RowOf row_of, const int32_t* s_prev, u32x4 (&w)[NCH],
+                                            const float (*s_w1)[NCH * 8], uint32_t (*s_key)[kMaxChains],
+                                            uint32_t (*s_bad)[kMaxChains], const uint16_t* __restrict__ base,
+                                            int64_t stride, int vc, bool live, int vocab, int tid) {
+  using R = RecBits<THREADS>;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int g = 0; g < n; g += kGroup) {
+    bool ok[kGroup];
+    uint32_t bv[kGroup];
+    int cs[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      cs[i] = min(g + i, n - 1);
+      const int p = s_prev[cs[i]];
+      ok[i] = p >= 0 && p < vocab;
+      // unconditional (a lane past the vocabulary reads the last token and
+      // is not scored), so no branch makes the compiler wait for it early
+      bv[i] = uint32_t(gload(base + int64_t(row_of(cs[i])) * stride + vc));
+    }
+
+    float acc[kGroup] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      // Keep W2 as raw bf16 pairs between groups (128 VGPRs): converting it
+      // once for every group would hold 256 floats and spill. The pin sits
+      // at each chunk's use, so chunk c waits for its own load only and the
+      // first chunks are scored while the later ones stream in.
+      asm volatile("" : "+v"(w[c]));
+      float f[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        f[2 * k] = bf16_lo(w[c][k]);
+        f[2 * k + 1] = bf16_hi(w[c][k]);
+      }
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        const float4 a = *reinterpret_cast<const float4*>(&s_w1[cs[i]][c * 8]);
+        const float4 b = *reinterpret_cast<const float4*>(&s_w1[cs[i]][c * 8 + 4]);
+        acc[i] = __builtin_fmaf(f[0], a.x, acc[i]);
+        acc[i] = __builtin_fmaf(f[1], a.y, acc[i]);
+        acc[i] = __builtin_fmaf(f[2], a.z, acc[i]);
+        acc[i] = __builtin_fmaf(f[3], a.w, acc[i]);
+        acc[i] = __builtin_fmaf(f[4], b.x, acc[i]);
+        acc[i] = __builtin_fmaf(f[5], b.y, acc[i]);
+        acc[i] = __builtin_fmaf(f[6], b.z, acc[i]);
+        acc[i] = __builtin_fmaf(f[7], b.w, acc[i]);
+      }
+    }
+
+    // The sums are pinned here, so the compiler cannot sink each chain's
+    // sum into the branch that uses it (which would split the shared loop);
+    // a slot past the last chain repeats it and is not stored.
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) asm volatile("" : "+v"(acc[i]));
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const uint32_t d = ok[i] ? f32_to_bf16(acc[i]) : 0u;
+      const uint32_t s = f32_to_bf16(bf16_to_f32(uint16_t(bv[i])) + __uint_as_float(d << 16));
+      const bool nonfinite = live && (s & 0x7F80u) == 0x7F80u;
+      const bool nan = (s & 0x7F80u) == 0x7F80u && (s & 0x7Fu) != 0u;
+      uint32_t key = (live && !nan) ? (order_key(s) << R::kLB) | uint32_t(THREADS - 1 - tid) : 0u;
+      key = wave_umax(key);
+      const bool bad = __any(nonfinite) || !ok[i];
+      if (lane == 0 && g + i < n) {
+        s_key[wave][g + i] = key;
+        s_bad[wave][g + i] = bad ? 1u : 0u;
+      }
+    }
+  }
 }
 
 // NCH = rank / 8, a compile-time count so that every chunk loop is straight
@@ -217,10 +308,10 @@ __global__ __launch_bounds__(kThreads, 2) void markov_scan(Step st, const uint16
   // The first chain apart from the loop below, so that its wait (on the
   // records only) is not merged with the reloads' waits (on everything).
   if (fold_first) {
-    fold_use(fa, fe, 0, lane);
+    fold_use<kThreads>(fa, fe, 0, lane);
     for (int b0 = 64 * 8; b0 < nblocks; b0 += 64 * 8) {
       fold_load(fe, prec + int64_t(wave) * nblocks, nblocks, b0, lane);
-      fold_use(fa, fe, b0, lane);
+      fold_use<kThreads>(fa, fe, b0, lane);
     }
     fold_done(wave, fa);
   }
@@ -229,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 2) void markov_scan(Step st, const uint16
     FoldAcc a{0u, 0u, false};
     for (int b0 = 0; b0 < nblocks; b0 += 64 * 8) {
       fold_load(fe, r, nblocks, b0, lane);
-      fold_use(a, fe, b0, lane);
+      fold_use<kThreads>(a, fe, b0, lane);
     }
     fold_done(ci, a);
   }
@@ -272,69 +363,8 @@ __global__ __launch_bounds__(kThreads, 2) void markov_scan(Step st, const uint16
   }
   __syncthreads();
 
-  for (int g = 0; g < st.n; g += kGroup) {
-    bool ok[kGroup];
-    uint32_t bv[kGroup];
-    int cs[kGroup];
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      cs[i] = min(g + i, st.n - 1);
-      const int p = s_prev[cs[i]];
-      ok[i] = p >= 0 && p < vocab;
-      // unconditional (a lane past the vocabulary reads the last token and
-      // is not scored), so no branch makes the compiler wait for it early
-      bv[i] = uint32_t(gload(base + int64_t(st.row[cs[i]]) * stride + vc));
-    }
-
-    float acc[kGroup] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      // Keep W2 as raw bf16 pairs between groups (128 VGPRs): converting it
-      // once for every group would hold 256 floats and spill. The pin sits
-      // at each chunk's use, so chunk c waits for its own load only and the
-      // first chunks are scored while the later ones stream in.
-      asm volatile("" : "+v"(w[c]));
-      float f[8];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        f[2 * k] = bf16_lo(w[c][k]);
-        f[2 * k + 1] = bf16_hi(w[c][k]);
-      }
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        const float4 a = *reinterpret_cast<const float4*>(&s_w1[cs[i]][c * 8]);
-        const float4 b = *reinterpret_cast<const float4*>(&s_w1[cs[i]][c * 8 + 4]);
-        acc[i] = __builtin_fmaf(f[0], a.x, acc[i]);
-        acc[i] = __builtin_fmaf(f[1], a.y, acc[i]);
-        acc[i] = __builtin_fmaf(f[2], a.z, acc[i]);
-        acc[i] = __builtin_fmaf(f[3], a.w, acc[i]);
-        acc[i] = __builtin_fmaf(f[4], b.x, acc[i]);
-        acc[i] = __builtin_fmaf(f[5], b.y, acc[i]);
-        acc[i] = __builtin_fmaf(f[6], b.z, acc[i]);
-        acc[i] = __builtin_fmaf(f[7], b.w, acc[i]);
-      }
-    }
-
-    // The sums are pinned here, so the compiler cannot sink each chain's
-    // sum into the branch that uses it (which would split the shared loop);
-    // a slot past the last chain repeats it and is not stored.
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) asm volatile("" : "+v"(acc[i]));
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      const uint32_t d = ok[i] ? f32_to_bf16(acc[i]) : 0u;
-      const uint32_t s = f32_to_bf16(bf16_to_f32(uint16_t(bv[i])) + __uint_as_float(d << 16));
-      const bool nonfinite = live && (s & 0x7F80u) == 0x7F80u;
-      const bool nan = (s & 0x7F80u) == 0x7F80u && (s & 0x7Fu) != 0u;
-      uint32_t key = (live && !nan) ? (order_key(s) << 8) | uint32_t(kThreads - 1 - tid) : 0u;
-      key = wave_umax(key);
-      const bool bad = __any(nonfinite) || !ok[i];
-      if (lane == 0 && g + i < st.n) {
-        s_key[wave][g + i] = key;
-        s_bad[wave][g + i] = bad ? 1u : 0u;
-      }
-    }
-  }
+  score_depth<NCH, kThreads>(st.n, [&](int i) { return st.row[i]; }, s_prev, w, s_w1, s_key, s_bad, base,
+                            stride, vc, live, vocab, tid);
   __syncthreads();
   if (tid < st.n) {
     uint32_t key = 0, bad = 0;
@@ -359,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void markov_fold(Step st, int nblocks,
     for (int b0 = 0; b0 < nblocks; b0 += 64 * 8) {
       uint32_t e[8];
       fold_load(e, r, nblocks, b0, lane);
-      fold_use(fa, e, b0, lane);
+      fold_use<kThreads>(fa, e, b0, lane);
     }
     uint32_t tok;
     bool bad;
@@ -369,6 +399,267 @@ __global__ __launch_bounds__(kThreads) void markov_fold(Step st, int nblocks,
       gstore(flag + st.prow[ci], uint8_t(bad ? 1 : 0));
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Resident form: the whole pass in one launch whose blocks all run at once,
+// each wave holding its 64-token tile of W2 in registers from the first
+// depth to the last, so W2 is read from HBM once a pass instead of once a
+// depth. Between depths the blocks exchange their records through the
+// workspace: a record is one 64-bit word whose upper half is its depth + 1,
+// written with a single device-scope store, so a block that reads the tag
+// it waits for has read that depth's record, with no other ordering
+// needed; the reader polls until every block's record carries the tag. The
+// records of one depth lie in the half of the workspace the next depth does
+// not write (depths alternate), and a block writes depth j + 2 only after it
+// read every block's depth j + 1, which each block wrote after it finished
+// reading depth j; so no record is overwritten while a block still waits
+// for it. The workspace is cleared by a small launch before each pass, so
+// no tag left by an earlier pass is taken for one of this pass. The
+// arithmetic is score_depth's, bit for bit the one-launch-a-depth form's.
+//
+// The launch is an ordinary one: the host admits the form only when every
+// block fits on the device at once (one 512-thread block a CU), so on a
+// device running nothing else all blocks start together. Other work on the
+// device can hold some blocks back; the others then wait, and a wait longer
+// than kWaitTicks abandons the pass (flag 2 from that depth on). A
+// cooperative launch would guarantee residency, but on this runtime it
+// waits on the host for the stream's earlier work and costs 15-20 us a
+// call on the device (measured: 112 against 93 us a pass).
+
+constexpr int kRThreads = 512;  // 8 waves, one block a CU (the W2 tiles take 128 VGPRs a lane)
+constexpr int kRWaves = kRThreads / 64;
+constexpr int kRMaxBlocks = 512;  // a fold reads at most 8 records a lane
+
+struct Chains {
+  int32_t n;          // chains
+  int32_t max_depth;  // the deepest chain's depth
+  int32_t row0[kMaxChains];
+  int32_t depth[kMaxChains];
+};
+
+// Chain c's records of one depth in one wave: polled until every block's
+// carries the tag, then folded. False when wait_ticks of the 100 MHz clock
+// passed with some record still missing (the pass is then abandoned).
+__device__ __forceinline__ bool fold_poll(const unsigned long long* __restrict__ rec, int nblocks,
+                                          uint32_t tag, int lane, uint64_t wait_ticks, uint32_t& tok,
+                                          bool& bad) {
+  uint32_t e[8];
+  uint64_t t0 = 0;
+  for (bool first = true;; first = false) {
+    // all eight loads in flight together (a lane past the last block reads
+    // the last block's record again), then the tests
+    unsigned long long x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      x[u] = __hip_atomic_load(rec + min(u * 64 + lane, nblocks - 1), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = true;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      ok &= uint32_t(x[u] >> 32) == tag;
+      e[u] = u * 64 + lane < nblocks ? uint32_t(x[u]) : 0u;
+    }
+    if (__all(ok)) break;
+    const uint64_t now = __builtin_amdgcn_s_memrealtime();
+    if (first) t0 = now;
+    else if (now - t0 > wait_ticks) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  FoldAcc a{0u, 0u, false};
+  fold_use<kRThreads>(a, e, 0, lane);
+  fold_finish(a, tok, bad);
+  return true;
+}
+
+template <int NCH>
+__global__ __launch_bounds__(kRThreads, 1) void markov_resident(
+    Chains ch, const uint16_t* __restrict__ base, int64_t stride, const int32_t* __restrict__ prev0,
+    const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w2c, int vocab, int nblocks,
+    unsigned long long* __restrict__ rec, int32_t* __restrict__ pick, uint8_t* __restrict__ flag,
+    uint64_t wait_ticks) {
+  constexpr int rank = NCH * 8;
+  __shared__ __attribute__((aligned(16))) float s_w1[kMaxChains][rank];
+  __shared__ uint32_t s_key[kRWaves][kMaxChains];
+  __shared__ uint32_t s_bad[kRWaves][kMaxChains];
+  __shared__ int32_t s_tok[kMaxChains];    // chain c's previous token
+  __shared__ int32_t s_row[kMaxChains];    // the depth's i-th chain: its row,
+  __shared__ int32_t s_prev[kMaxChains];   // its previous token
+  __shared__ int32_t s_chain[kMaxChains];  // and its chain
+  __shared__ int32_t s_fail;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int v = blockIdx.x * kRThreads + tid;
+  const bool live = v < vocab;
+  const int vc = live ? v : vocab - 1;
+  const size_t half = size_t(kMaxChains) * nblocks;
+
+  // W1 rows of the depth's chains in float32 into LDS (row 0 stands in for
+  // an invalid token): piece idx = tid + k * kRThreads is chunk idx % NCH of
+  // the row of the depth's chain idx / NCH; loads first, then conversions
+  constexpr int kRPass = (kMaxChains * NCH + kRThreads - 1) / kRThreads;
+  auto w1_load = [&](u32x4(&q)[kRPass], int n, auto prev_of) {
+#pragma unroll
+    for (int k = 0; k < kRPass; ++k) {
+      // unconditional (a piece past the last repeats it), so that no branch
+      // makes the compiler wait for the load at once
+      const int idx = min(tid + k * kRThreads, n * NCH - 1);
+      const int i = idx / NCH;
+      const int p = prev_of(k, i);
+      const bool ok = p >= 0 && p < vocab;
+      q[k] = load16(w1 + int64_t(ok ? p : 0) * rank + (idx - i * NCH) * 8);
+    }
+  };
+  auto w1_store = [&](const u32x4(&q)[kRPass], int n) {
+#pragma unroll
+    for (int k = 0; k < kRPass; ++k) {
+      const int idx = tid + k * kRThreads;
+      if (idx < n * NCH) {
+        const int i = idx / NCH;
+        const int c = idx - i * NCH;
+        float4 a, b;
+        a.x = bf16_lo(q[k][0]); a.y = bf16_hi(q[k][0]); a.z = bf16_lo(q[k][1]); a.w = bf16_hi(q[k][1]);
+        b.x = bf16_lo(q[k][2]); b.y = bf16_hi(q[k][2]); b.z = bf16_lo(q[k][3]); b.w = bf16_hi(q[k][3]);
+        *reinterpret_cast<float4*>(&s_w1[i][c * 8]) = a;
+        *reinterpret_cast<float4*>(&s_w1[i][c * 8 + 4]) = b;
+      }
+    }
+  };
+
+  // Depth 0 scores every chain, in chain order. Its previous tokens (one
+  // round trip) and then its W1 rows are requested before W2, so that depth
+  // 0 waits for W2 only where it scores (loads retire in issue order).
+  const int n0 = ch.n;
+  int32_t pq[kRPass];
+#pragma unroll
+  for (int k = 0; k < kRPass; ++k) pq[k] = gload(prev0 + min((tid + k * kRThreads) / NCH, n0 - 1));
+  u32x4 q[kRPass];
+  w1_load(q, n0, [&](int k, int) { return pq[k]; });
+  __builtin_amdgcn_sched_barrier(0);
+  // the wave's W2 tile, kept in registers for the whole pass
+  u32x4 w[NCH];
+  const int64_t tile = vc / 64;
+  const int64_t tl = min(int64_t(64), int64_t(vocab) - tile * 64);
+  const uint16_t* wp = w2c + tile * 64 * rank + (vc - tile * 64) * 8;
+  const int64_t plane = tl * 8;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) w[c] = load16(wp + c * plane);
+  __builtin_amdgcn_sched_barrier(0);
+  // chain i's token from the thread that loaded its chunk 0 (already waited
+  // for: its W1 address depends on it)
+#pragma unroll
+  for (int k = 0; k < kRPass; ++k) {
+    const int idx = tid + k * kRThreads;
+    if (idx < n0 * NCH && idx % NCH == 0) {
+      s_tok[idx / NCH] = pq[k];
+      s_prev[idx / NCH] = pq[k];
+    }
+  }
+  if (tid == 0) {
+    s_fail = 0;
+    for (int c = 0; c < n0; ++c) {
+      s_chain[c] = c;
+      s_row[c] = ch.row0[c];
+    }
+  }
+  w1_store(q, n0);
+
+  for (int j = 0; j < ch.max_depth; ++j) {
+    int n = n0;
+    if (j > 0) {
+      // depth j - 1's picks: every block folds the chains that go on (wave w
+      // the w-th, (w + 8)-th, ... of them), block 0 also the chains that end
+      // there, and block 0 writes the picks and flags
+      const unsigned long long* r = rec + size_t((j - 1) & 1) * half;
+      int k = 0;
+      bool failed = false;
+      for (int c = 0; c < ch.n; ++c) {
+        const bool need = ch.depth[c] > j || (blockIdx.x == 0 && ch.depth[c] == j);
+        if (!need) continue;
+        if (k++ % kRWaves != wave || failed) continue;
+        uint32_t tok = 0;
+        bool bad = false;
+        if (!fold_poll(r + size_t(c) * nblocks, nblocks, uint32_t(j), lane, wait_ticks, tok, bad)) {
+          failed = true;
+          if (lane == 0) s_fail = 1;
+          continue;
+        }
+        if (lane == 0) {
+          s_tok[c] = int32_t(tok);
+          if (blockIdx.x == 0) {
+            gstore(pick + ch.row0[c] + j - 1, int32_t(tok));
+            gstore(flag + ch.row0[c] + j - 1, uint8_t(bad ? 1 : 0));
+          }
+        }
+      }
+      __syncthreads();
+      if (s_fail != 0) {
+        // abandoned: block 0 marks every row from depth j - 1 on with flag 2
+        if (blockIdx.x == 0 && tid < ch.n)
+          for (int d = j - 1; d < ch.depth[tid]; ++d) gstore(flag + ch.row0[tid] + d, uint8_t(2));
+        return;
+      }
+
+      // the chains scored at this depth, in chain order
+      n = 0;
+      for (int c = 0; c < ch.n; ++c) n += ch.depth[c] > j ? 1 : 0;
+      if (tid == 0) {
+        int i = 0;
+        for (int c = 0; c < ch.n; ++c)
+          if (ch.depth[c] > j) {
+            s_chain[i] = c;
+            s_row[i] = ch.row0[c] + j;
+            s_prev[i] = s_tok[c];
+            ++i;
+          }
+      }
+      __syncthreads();
+      w1_load(q, n, [&](int, int i) { return s_prev[i]; });
+      w1_store(q, n);
+    }
+    __syncthreads();
+
+    n = __builtin_amdgcn_readfirstlane(n);  // uniform: a scalar loop count
+    score_depth<NCH, kRThreads>(n, [&](int i) { return s_row[i]; }, s_prev, w, s_w1, s_key, s_bad, base,
+                                stride, vc, live, vocab, tid);
+    __syncthreads();
+    if (tid < n) {
+      uint32_t key = 0, bad = 0;
+#pragma unroll
+      for (int wv = 0; wv < kRWaves; ++wv) {
+        key = s_key[wv][tid] > key ? s_key[wv][tid] : key;
+        bad |= s_bad[wv][tid];
+      }
+      const unsigned long long word =
+          (static_cast<unsigned long long>(j + 1) << 32) | key | (bad ? kRecBad : 0u);
+      __hip_atomic_store(rec + size_t(j & 1) * half + size_t(s_chain[tid]) * nblocks + blockIdx.x, word,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // the deepest depth's picks, block 0 alone
+  if (blockIdx.x != 0) return;
+  const int j = ch.max_depth;
+  const unsigned long long* r = rec + size_t((j - 1) & 1) * half;
+  int k = 0;
+  for (int c = 0; c < ch.n; ++c) {
+    if (ch.depth[c] != j) continue;
+    if (k++ % kRWaves != wave) continue;
+    uint32_t tok = 0;
+    bool bad = false;
+    const bool done = fold_poll(r + size_t(c) * nblocks, nblocks, uint32_t(j), lane, wait_ticks, tok, bad);
+    if (lane == 0) {
+      gstore(pick + ch.row0[c] + j - 1, int32_t(done ? tok : 0u));
+      gstore(flag + ch.row0[c] + j - 1, uint8_t(done ? (bad ? 1 : 0) : 2));
+    }
+  }
+}
+
+// Zeroes n 64-bit words (the resident form's records before a pass).
+__global__ __launch_bounds__(kThreads) void markov_clear(unsigned long long* __restrict__ p, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n) p[i] = 0ull;
 }
 
 // W2 [vocab][rank] -> tiles of 64 tokens, each [rank/8][tl][8] (tl = the
@@ -396,6 +687,46 @@ constexpr auto scan_table(std::integer_sequence<int, N...>) {
 // scan_for[rank / 8 - 1]
 constexpr auto scan_for = scan_table(std::make_integer_sequence<int, kMaxChunks>{});
 
+int64_t resident_blocks(int64_t vocab) { return (vocab + kRThreads - 1) / kRThreads; }
+
+typedef void (*ResidentFn)(Chains, const uint16_t*, int64_t, const int32_t*, const uint16_t*, const uint16_t*,
+                           int, int, unsigned long long*, int32_t*, uint8_t*, uint64_t);
+
+template <int... N>
+constexpr auto resident_table(std::integer_sequence<int, N...>) {
+  return std::array<ResidentFn, sizeof...(N)>{{&markov_resident<N + 1>...}};
+}
+// resident_for[rank / 8 - 1]
+constexpr auto resident_for = resident_table(std::make_integer_sequence<int, kMaxChunks>{});
+
+// How long a resident-form block waits for a record before it gives the
+// pass up: one second of the 100 MHz clock (an exchange takes a few us).
+constexpr uint64_t kWaitTicks = 100000000ull;
+
+// How many resident-form blocks the current device holds at once for this
+// rank; asked once per device and rank, kept as value + 1 so that 0 means
+// not asked yet.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_resident_cap[kMaxDevices][kMaxChunks];
+
+int resident_capacity(int nch) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::atomic<int>& slot = g_resident_cap[dev][nch - 1];
+  int v = slot.load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0, per = 0;
+    int cap = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per, reinterpret_cast<const void*>(resident_for[nch - 1]), kRThreads, 0) == hipSuccess)
+      cap = cus * per;
+    v = cap + 1;
+    slot.store(v, std::memory_order_relaxed);
+  }
+  return v - 1;
+}
+
 bool rank_ok(int32_t rank) { return rank >= 8 && rank <= ASV_MARKOV_MAX_RANK && rank % 8 == 0; }
 
 }  // namespace
@@ -403,8 +734,11 @@ bool rank_ok(int32_t rank) { return rank >= 8 && rank <= ASV_MARKOV_MAX_RANK && 
 
 extern "C" size_t asv_markov_workspace(int64_t vocab) {
   if (vocab < 1 || vocab > (int64_t(1) << 30)) return 0;
-  // two halves (depths alternate), each a record per chain and scan block
-  return 2 * size_t(asv::scan_blocks(vocab)) * asv::kMaxChains * sizeof(uint32_t);
+  // two halves (depths alternate), each a record per chain and block: 4 bytes
+  // a 256-token block for one launch a depth, 8 a 512-token block resident
+  const size_t launches = 2 * size_t(asv::scan_blocks(vocab)) * asv::kMaxChains * sizeof(uint32_t);
+  const size_t resident = 2 * size_t(asv::resident_blocks(vocab)) * asv::kMaxChains * sizeof(uint64_t);
+  return launches > resident ? launches : resident;
 }
 
 extern "C" int asv_markov_pack_w2(const uint16_t* w2, int64_t vocab, int32_t rank, uint16_t* w2c,
@@ -422,11 +756,12 @@ extern "C" int asv_markov_pack_w2(const uint16_t* w2, int64_t vocab, int32_t ran
   return hipGetLastError() == hipSuccess ? ASV_OK : ASV_E_HIP;
 }
 
-extern "C" int asv_markov_pick(const uint16_t* base, int64_t rows, int64_t row_stride,
-                               const asv_markov_chain* chains, int32_t n_chains, const int32_t* prev0,
-                               const uint16_t* w1, const uint16_t* w2c, int64_t vocab, int32_t rank,
-                               int32_t* pick, uint8_t* flag, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+extern "C" int asv_markov_pick_form(const uint16_t* base, int64_t rows, int64_t row_stride,
+                                    const asv_markov_chain* chains, int32_t n_chains, const int32_t* prev0,
+                                    const uint16_t* w1, const uint16_t* w2c, int64_t vocab, int32_t rank,
+                                    int32_t* pick, uint8_t* flag, void* workspace, size_t workspace_bytes,
+                                    int32_t form, void* stream) {
+  if (form != ASV_MARKOV_AUTO && form != ASV_MARKOV_LAUNCHES && form != ASV_MARKOV_RESIDENT) return ASV_E_ARG;
   if (n_chains < 0 || n_chains > ASV_MARKOV_MAX_CHAINS || rows < 0 || rows > INT_MAX)
     return ASV_E_SHAPE;
   if (vocab < 1 || vocab > (int64_t(1) << 30) || row_stride < vocab) return ASV_E_SHAPE;
@@ -453,6 +788,29 @@ extern "C" int asv_markov_pick(const uint16_t* base, int64_t rows, int64_t row_s
   if (workspace_bytes < asv_markov_workspace(vocab)) return ASV_E_CAPACITY;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // one resident launch when every block of it fits on the device at once
+  const int64_t nres = asv::resident_blocks(vocab);
+  const bool fits = nres <= asv::kRMaxBlocks && nres <= asv::resident_capacity(rank / 8);
+  if (form == ASV_MARKOV_RESIDENT && !fits) return ASV_E_UNSUPPORTED;
+  if (form != ASV_MARKOV_LAUNCHES && fits) {
+    asv::Chains ch{};
+    ch.n = n_chains;
+    ch.max_depth = max_depth;
+    for (int i = 0; i < n_chains; ++i) {
+      ch.row0[i] = chains[i].row0;
+      ch.depth[i] = chains[i].depth;
+    }
+    unsigned long long* rec = static_cast<unsigned long long*>(workspace);
+    const int64_t words = 2 * int64_t(asv::kMaxChains) * nres;
+    hipLaunchKernelGGL(asv::markov_clear, dim3(unsigned((words + asv::kThreads - 1) / asv::kThreads)),
+                       dim3(asv::kThreads), 0, st, rec, words);
+    if (hipGetLastError() != hipSuccess) return ASV_E_HIP;
+    hipLaunchKernelGGL(asv::resident_for[rank / 8 - 1], dim3(unsigned(nres)), dim3(asv::kRThreads), 0, st, ch,
+                       base, row_stride, prev0, w1, w2c, int(vocab), int(nres), rec, pick, flag, asv::kWaitTicks);
+    return hipGetLastError() == hipSuccess ? ASV_OK : ASV_E_HIP;
+  }
+
   const int nblocks = int(asv::scan_blocks(vocab));
   uint32_t* half[2] = {static_cast<uint32_t*>(workspace),
                        static_cast<uint32_t*>(workspace) + int64_t(nblocks) * asv::kMaxChains};
@@ -485,4 +843,13 @@ extern "C" int asv_markov_pick(const uint16_t* base, int64_t rows, int64_t row_s
                      half[(max_depth - 1) & 1], pick, flag);
   if (hipGetLastError() != hipSuccess) return ASV_E_HIP;
   return ASV_OK;
+}
+
+extern "C" int asv_markov_pick(const uint16_t* base, int64_t rows, int64_t row_stride,
+                               const asv_markov_chain* chains, int32_t n_chains, const int32_t* prev0,
+                               const uint16_t* w1, const uint16_t* w2c, int64_t vocab, int32_t rank,
+                               int32_t* pick, uint8_t* flag, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return asv_markov_pick_form(base, rows, row_stride, chains, n_chains, prev0, w1, w2c, vocab, rank, pick,
+                              flag, workspace, workspace_bytes, ASV_MARKOV_AUTO, stream);
 }

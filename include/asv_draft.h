@@ -94,12 +94,27 @@ int asv_draft_ids(const asv_draft_span* spans, int32_t n_streams, const int32_t*
  *              t = v / 64 (asv_markov_pack_w2); vocab * rank elements
  *   pick, flag device, int32 / uint8 [rows]
  *   workspace  device, asv_markov_workspace(vocab) bytes, 16-byte aligned;
- *              one call at a time per workspace (two halves of one 4-byte
- *              record per chain and 256-token block, depths alternating)
- * One launch a depth plus one on `stream`: the launch of depth j + 1 folds
- * depth j's block records for its previous tokens (its block 0 writes
- * depth j's picks and flags), and the last launch folds the deepest depth;
- * the host never reads a pick.
+ *              one call at a time per workspace (two halves of block
+ *              records, depths alternating)
+ * Two forms on `stream`, the same bits from either (asv_markov_pick_form
+ * chooses; asv_markov_pick takes ASV_MARKOV_AUTO):
+ *   resident: a clearing launch and one launch of 512-token blocks that
+ *     all run at once, each wave keeping its 64 tokens of W2 in registers
+ *     for every depth (W2 read once a pass); the blocks trade depth-tagged
+ *     8-byte records through the workspace between depths. Admitted when
+ *     ceil(vocab / 512) <= 512 and every block fits on the device at once
+ *     (one a CU: vocab <= 131,072 at rank 256 on a 256-CU device). Its
+ *     blocks wait for each other, so it needs them all running together:
+ *     run one resident pass at a time on a device (order calls made on
+ *     different streams), and expect other work on the device to delay
+ *     it. A block that waits more than a second for a record abandons the
+ *     pass: flag 2 on every row of the depth it waited for and the later
+ *     ones (pick then undefined there).
+ *   launches: one launch a depth plus one: the launch of depth j + 1 folds
+ *     depth j's 4-byte block records (256-token blocks) for its previous
+ *     tokens (its block 0 writes depth j's picks and flags), and the last
+ *     launch folds the deepest depth; W2 is read once a depth.
+ * The host never reads a pick.
  * Errors: ASV_E_SHAPE (n_chains > ASV_MARKOV_MAX_CHAINS, a depth outside
  * 1..ASV_MARKOV_MAX_DEPTH, a chain outside [0, rows) or two chains sharing a
  * row, vocab < 1 or > 2^30, row_stride < vocab); ASV_E_UNSUPPORTED (rank not
@@ -112,6 +127,20 @@ int asv_markov_pick(const uint16_t* base, int64_t rows, int64_t row_stride,
                     const uint16_t* w1, const uint16_t* w2c, int64_t vocab, int32_t rank,
                     int32_t* pick, uint8_t* flag, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* asv_markov_pick with its form chosen: ASV_MARKOV_AUTO (resident when it
+ * is admitted, else launches), ASV_MARKOV_LAUNCHES, or ASV_MARKOV_RESIDENT
+ * (ASV_E_UNSUPPORTED when not admitted on this device and rank).
+ * Defines: as asv_markov_pick. Errors: as asv_markov_pick, and ASV_E_ARG for
+ * an unknown form. */
+#define ASV_MARKOV_AUTO 0
+#define ASV_MARKOV_LAUNCHES 1
+#define ASV_MARKOV_RESIDENT 2
+int asv_markov_pick_form(const uint16_t* base, int64_t rows, int64_t row_stride,
+                         const asv_markov_chain* chains, int32_t n_chains, const int32_t* prev0,
+                         const uint16_t* w1, const uint16_t* w2c, int64_t vocab, int32_t rank,
+                         int32_t* pick, uint8_t* flag, void* workspace, size_t workspace_bytes,
+                         int32_t form, void* stream);
 
 /* W2 [vocab][rank] (row-major bf16, as the checkpoint holds it) into the
  * tiled layout asv_markov_pick reads; once, when the weights load.

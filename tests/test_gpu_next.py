@@ -93,7 +93,7 @@ def _bf16(rng, shape, scale=1.0):
     return (x.view(np.uint32) >> 16).astype(np.uint16)
 
 
-def _markov_gpu(base, chains, prev0, w1, w2, fill_pick=-7, fill_flag=9):
+def _markov_gpu(base, chains, prev0, w1, w2, fill_pick=-7, fill_flag=9, form=None):
     rows, vocab = base.shape
     rank = w1.shape[1]
     B = _dev(base.view(np.int16), torch.int16)
@@ -105,7 +105,7 @@ def _markov_gpu(base, chains, prev0, w1, w2, fill_pick=-7, fill_flag=9):
     pick = torch.full((rows,), fill_pick, dtype=torch.int32, device="cuda")
     flag = torch.full((rows,), fill_flag, dtype=torch.uint8, device="cuda")
     ws = torch.empty(asv.markov_workspace(vocab), dtype=torch.uint8, device="cuda")
-    asv.markov_pick(B, rows, vocab, chains, P0, W1, W2c, vocab, rank, pick, flag, ws)
+    asv.markov_pick(B, rows, vocab, chains, P0, W1, W2c, vocab, rank, pick, flag, ws, form=form)
     torch.cuda.synchronize()
     return pick.cpu().numpy(), flag.cpu().numpy()
 
@@ -118,9 +118,14 @@ def _markov_ref(base, chains, prev0, w1, w2, fill_pick=-7, fill_flag=9):
     return pick, flag
 
 
-def _check_markov(base, chains, prev0, w1, w2):
-    print(f"markov case: vocab {base.shape[1]} rank {w1.shape[1]} chains {chains}", flush=True)
-    gp, gf = _markov_gpu(base, chains, prev0, w1, w2)
+# Both forms of the pass (one launch a depth; one resident launch) on every
+# case below; "auto" is what asv_markov_pick takes.
+FORMS = ["launches", "resident"]
+
+
+def _check_markov(base, chains, prev0, w1, w2, form="auto"):
+    print(f"markov case ({form}): vocab {base.shape[1]} rank {w1.shape[1]} chains {chains}", flush=True)
+    gp, gf = _markov_gpu(base, chains, prev0, w1, w2, form=form)
     rp, rf = _markov_ref(base, chains, prev0, w1, w2)
     assert np.array_equal(gp, rp), (gp, rp)
     assert np.array_equal(gf, rf), (gf, rf)
@@ -142,13 +147,14 @@ def test_markov_pack_is_the_tiled_layout():
         assert np.array_equal(W2c.cpu().numpy().view(np.uint16).reshape(-1), want)
 
 
-def test_markov_full_shape_parity():
+@pytest.mark.parametrize("form", FORMS + ["auto"])
+def test_markov_full_shape_parity(form):
     """vocabulary 128,000, rank 256: three chains of depths 3, 2, 1."""
     rng = np.random.default_rng(12)
     vocab, rank = 128000, 256
     w1, w2 = _bf16(rng, (vocab, rank), 0.3), _bf16(rng, (vocab, rank), 0.3)
     base = _bf16(rng, (6, vocab), 3.0)
-    _check_markov(base, [(0, 3), (3, 2), (5, 1)], [17, 127999, 5000], w1, w2)
+    _check_markov(base, [(0, 3), (3, 2), (5, 1)], [17, 127999, 5000], w1, w2, form)
 
 
 @pytest.mark.parametrize("vocab,rank,chains", [
@@ -162,27 +168,71 @@ def test_markov_full_shape_parity():
     (4099, 136, [(0, 9), (9, 9), (18, 9)]),                           # the drafter's depth
     (3000, 256, [(0, 16)]),                                           # the longest chain
 ])
-def test_markov_ragged_parity(vocab, rank, chains):
+@pytest.mark.parametrize("form", FORMS)
+def test_markov_ragged_parity(vocab, rank, chains, form):
     rng = np.random.default_rng(vocab * 7 + rank)
     rows = max(r + d for r, d in chains) + 1
     w1, w2 = _bf16(rng, (vocab, rank), 0.5), _bf16(rng, (vocab, rank), 0.5)
     base = _bf16(rng, (rows, vocab), 2.0)
     prev0 = rng.integers(0, vocab, len(chains))
-    gp, gf = _check_markov(base, chains, prev0, w1, w2)
+    gp, gf = _check_markov(base, chains, prev0, w1, w2, form)
     assert gp[-1] == -7 and gf[-1] == 9                               # a row in no chain
 
 
 def test_markov_large_vocabulary():
     """2,344 scan blocks a depth (vocab 600,000 at rank 8): the fold reads
-    its records in several rounds of eight a lane."""
+    its records in several rounds of eight a lane. 1,172 blocks of 512
+    tokens are more than the resident form takes: it is refused, and the
+    automatic choice runs one launch a depth."""
     rng = np.random.default_rng(15)
     vocab, rank = 600000, 8
     w1, w2 = _bf16(rng, (vocab, rank), 0.5), _bf16(rng, (vocab, rank), 0.5)
     base = _bf16(rng, (4, vocab), 2.0)
     _check_markov(base, [(0, 3)], [123456], w1, w2)
+    with pytest.raises(asv.AsvError) as refused:
+        _markov_gpu(base, [(0, 3)], [123456], w1, w2, form="resident")
+    assert refused.value.code == -3                                   # ASV_E_UNSUPPORTED
 
 
-def test_markov_planted_nonfinite_and_invalid_tokens():
+@pytest.mark.parametrize("form", FORMS)
+def test_markov_largest_resident_vocabulary(form):
+    """131,072 tokens at rank 256: 256 blocks of 512, one a CU, the most the
+    resident form holds on a 256-CU device (the automatic choice takes it)."""
+    rng = np.random.default_rng(16)
+    vocab, rank = 131072, 256
+    w1, w2 = _bf16(rng, (vocab, rank), 0.3), _bf16(rng, (vocab, rank), 0.3)
+    base = _bf16(rng, (5, vocab), 3.0)
+    _check_markov(base, [(0, 4), (4, 1)], [131071, 0], w1, w2, form)
+
+
+def test_markov_resident_back_to_back_calls():
+    """Two resident passes in a row on one workspace, the second with fewer
+    chains and depths: the records of the first (tags up to its depth) must
+    not be taken for the second's."""
+    rng = np.random.default_rng(17)
+    vocab, rank = 20000, 64
+    w1, w2 = _bf16(rng, (vocab, rank), 0.5), _bf16(rng, (vocab, rank), 0.5)
+    base = _bf16(rng, (24, vocab), 2.0)
+    W1 = _dev(w1.view(np.int16), torch.int16)
+    W2 = _dev(w2.view(np.int16), torch.int16)
+    W2c = torch.empty_like(W2)
+    asv.markov_pack_w2(W2, vocab, rank, W2c)
+    B = _dev(base.view(np.int16), torch.int16)
+    ws = torch.empty(asv.markov_workspace(vocab), dtype=torch.uint8, device="cuda")
+    for chains, prev0 in [([(0, 8), (8, 8), (16, 8)], [5, 6, 7]), ([(3, 2)], [19999])]:
+        print(f"markov back to back: chains {chains}", flush=True)
+        P0 = _dev(np.asarray(prev0, dtype=np.int32), torch.int32)
+        pick = torch.full((24,), -7, dtype=torch.int32, device="cuda")
+        flag = torch.full((24,), 9, dtype=torch.uint8, device="cuda")
+        asv.markov_pick(B, 24, vocab, chains, P0, W1, W2c, vocab, rank, pick, flag, ws, form="resident")
+        torch.cuda.synchronize()
+        rp, rf = _markov_ref(base, chains, prev0, w1, w2)
+        assert np.array_equal(pick.cpu().numpy(), rp)
+        assert np.array_equal(flag.cpu().numpy(), rf)
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_markov_planted_nonfinite_and_invalid_tokens(form):
     rng = np.random.default_rng(13)
     vocab, rank = 5000, 64
     w1, w2 = _bf16(rng, (vocab, rank), 0.5), _bf16(rng, (vocab, rank), 0.5)
@@ -194,12 +244,13 @@ def test_markov_planted_nonfinite_and_invalid_tokens():
     base[3, :] = QNAN                                   # no real score: pick 0
     chains = [(0, 4), (4, 2), (6, 2), (8, 2)]
     prev0 = [3, -1, vocab, 2**31 - 1]                   # three invalid first tokens
-    gp, gf = _check_markov(base, chains, prev0, w1, w2)
+    gp, gf = _check_markov(base, chains, prev0, w1, w2, form)
     assert gf[[0, 1, 3, 4, 6, 8]].tolist() == [1] * 6
     assert gp[1] == 4000 and gp[3] == 0
 
 
-def test_markov_subnormal_products():
+@pytest.mark.parametrize("form", FORMS)
+def test_markov_subnormal_products(form):
     """Weights near 2^-64: the products lie near or below float32's smallest
     normal 2^-126, so a flush to zero anywhere would change the sums, while
     the sums (near 2^-125) keep enough bf16 steps to tell scores apart."""
@@ -208,10 +259,11 @@ def test_markov_subnormal_products():
     tiny = 2.0 ** -64
     w1, w2 = _bf16(rng, (vocab, rank), tiny), _bf16(rng, (vocab, rank), tiny)
     base = np.zeros((4, vocab), dtype=np.uint16)
-    _check_markov(base, [(0, 4)], [9], w1, w2)
+    _check_markov(base, [(0, 4)], [9], w1, w2, form)
 
 
-def test_markov_ties_go_to_the_lowest_token():
+@pytest.mark.parametrize("form", FORMS)
+def test_markov_ties_go_to_the_lowest_token(form):
     vocab, rank = 3000, 8
     w1 = np.zeros((vocab, rank), dtype=np.uint16)
     w2 = np.zeros((vocab, rank), dtype=np.uint16)
@@ -220,5 +272,5 @@ def test_markov_ties_go_to_the_lowest_token():
         base[0, t] = 0x4000                             # 2.0
     base[1, :] = 0x8000                                 # -0 everywhere: ties with +0
     base[1, 2500] = 0x0000
-    gp, gf = _check_markov(base, [(0, 2)], [1], w1, w2)
+    gp, gf = _check_markov(base, [(0, 2)], [1], w1, w2, form)
     assert gp.tolist() == [257, 0] and gf.tolist() == [0, 0]
