@@ -198,10 +198,13 @@ def cpu_baseline(rnd, R, full=False):
 def markov_leg(torch, asv, dev, seed, calls=20):
     """One Markov-head pass of the drafter: 4 chains x depth 8 (a hold pass
     holds at most 32 rows), vocabulary 128,000, rank 256, random bf16
-    weights. Each depth reads all of W2 once (every chain at that depth
-    shares it) plus each chain's logit row; the W1 rows are 512 bytes each."""
+    weights, in the form asv_markov_pick chooses (resident: W2 read once a
+    pass and kept in registers) and, for comparison, one launch a depth (W2
+    read once a depth). Bytes of the chosen form: W2 once, each chain's
+    logit rows, the W1 rows (512 bytes each); its arithmetic: one float32
+    fused multiply-add per token, rank index, chain and depth."""
     vocab, rank, chains = 128000, 256, [(0, 8), (8, 8), (16, 8), (24, 8)]
-    rows = 32
+    rows, depth = 32, 8
     g = torch.Generator(device=dev)
     g.manual_seed(seed + 101)
 
@@ -217,25 +220,36 @@ def markov_leg(torch, asv, dev, seed, calls=20):
     flag = torch.empty(rows, dtype=torch.uint8, device=dev)
     ws = torch.empty(asv.markov_workspace(vocab), dtype=torch.uint8, device=dev)
 
-    def call():
-        asv.markov_pick(base, rows, vocab, chains, prev0, w1, w2c, vocab, rank, pick, flag, ws)
+    def timed(form):
+        def call():
+            asv.markov_pick(base, rows, vocab, chains, prev0, w1, w2c, vocab, rank, pick, flag, ws, form=form)
+        for _ in range(3):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(calls):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / calls
 
-    for _ in range(3):
-        call()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(calls):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / calls
-    depth = 8
-    nbytes = depth * vocab * rank * 2 + rows * vocab * 2 + rows * rank * 2
-    return {"shape": "4 chains x depth 8, vocab 128,000, rank 256", "avg_call_us": us,
-            "launches_per_call": depth + 1, "bytes_per_call": nbytes,
+    us_launches = timed("launches")
+    launches_bytes = depth * vocab * rank * 2 + rows * vocab * 2 + rows * rank * 2
+    try:                             # the form asv_markov_pick takes when the device admits it
+        us, form, n_launch = timed("resident"), "resident", 2
+        nbytes = vocab * rank * 2 + rows * vocab * 2 + rows * rank * 2
+    except asv.AsvError:
+        us, form, n_launch, nbytes = us_launches, "launches", depth + 1, launches_bytes
+    fmas = depth * vocab * rank * len(chains)
+    fma_peak = 256 * 64 * 2.4e9      # non-packed float32 FMA lanes of 256 CUs at 2.4 GHz
+    return {"shape": "4 chains x depth 8, vocab 128,000, rank 256", "form": form,
+            "avg_call_us": us, "launches_per_call": n_launch, "bytes_per_call": nbytes,
             "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
-            "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+            "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "fmas_per_call": fmas, "fma_frac": fmas / (us * 1e-6) / fma_peak,
+            "launches_form_avg_call_us": us_launches,
+            "launches_form_bytes_per_call": launches_bytes}
 
 
 def measure_round(torch, asv, workloads, dev, config, steps, warmup, block=False, with_qk=False,
