@@ -383,7 +383,7 @@ def workload_entry(m):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
