@@ -205,6 +205,18 @@ def test_markov_largest_resident_vocabulary(form):
     _check_markov(base, [(0, 4), (4, 1)], [131071, 0], w1, w2, form)
 
 
+@pytest.mark.parametrize("form", FORMS)
+def test_markov_most_resident_blocks(form):
+    """262,144 tokens at rank 8: 512 blocks of 512, the most the resident
+    form takes (several a CU at this rank), so each fold reads eight
+    records a lane."""
+    rng = np.random.default_rng(18)
+    vocab, rank = 262144, 8
+    w1, w2 = _bf16(rng, (vocab, rank), 0.5), _bf16(rng, (vocab, rank), 0.5)
+    base = _bf16(rng, (6, vocab), 2.0)
+    _check_markov(base, [(0, 3), (3, 2)], [262143, 77], w1, w2, form)
+
+
 def test_markov_resident_back_to_back_calls():
     """Two resident passes in a row on one workspace, the second with fewer
     chains and depths: the records of the first (tags up to its depth) must
