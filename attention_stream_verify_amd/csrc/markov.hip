@@ -12,6 +12,11 @@
 // arithmetic (float32 dot, k ascending, one rounding per term) is written
 // out in include/asv_draft.h.
 //
+// Two forms of a pass, the same bits from either: a resident form (one
+// launch for the whole pass, W2 kept in registers; further below, where its
+// kernel is) taken whenever its blocks fit on the device at once, and the
+// form described here, one launch a depth.
+//
 // A pass of depth D is D scan launches and one fold launch, no atomics.
 // The scan of depth j scores every chain's row at that depth and leaves,
 // per chain, one 4-byte record a block (its best order key and lane, and a
