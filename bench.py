@@ -345,11 +345,32 @@ def measure_round(torch, asv, workloads, dev, config, steps, warmup, block=False
         torch.cuda.synchronize()
         ms_step = g0.elapsed_time(g1) / steps
         del graph
+        # the attention launches alone, every layer in one captured graph and
+        # replayed: kernel time without the host's per-launch latency, which
+        # the eager events above include for short launches
+        agraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(agraph):
+            for i in range(rnd.n_attn):
+                rb.attn(i, rb.q if with_qk else rnd.attn[i][0])
+        for _ in range(warmup):
+            agraph.replay()
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(steps):
+            agraph.replay()
+        a1.record()
+        torch.cuda.synchronize()
+        attn_graph_us = a0.elapsed_time(a1) / (steps * rnd.n_attn) * 1e3
+        del agraph
+    else:
+        attn_graph_us = None
     return {
         "rnd": rnd, "rb": rb, "R": R, "S": S, "sum_keys": sum_keys, "attn_bytes": attn_bytes,
         "attn_flops": attn_flops, "merge_bytes": merge_bytes, "qkv": (qkv, gq, gk),
         "ms_step": ms_step, "eager_ms_step": eager_ms_step, "round_ms": round_ms,
         "attn_us": sum(attn_ms) / len(attn_ms) * 1e3, "pair_us": sum(pair_ms) / len(pair_ms) * 1e3,
+        "attn_graph_us": attn_graph_us,
     }
 
 
@@ -377,6 +398,9 @@ def workload_entry(m):
         "attn_flops": m["attn_flops"], "attn_bound_us": bound, "attn_frac_of_bound": bound / m["attn_us"],
         "attn_merge_us": m["pair_us"],
         "attn_merge_frac_hbm": pair_bytes / (m["pair_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "attn_graph_us": m["attn_graph_us"],
+        "attn_graph_frac_hbm": (None if m["attn_graph_us"] is None
+                                else m["attn_bytes"] / (m["attn_graph_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS),
     }
 
 
@@ -483,6 +507,8 @@ def main():
             "flops_per_launch": attn_flops,
             "mfma_frac": attn_flops / (attn_avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "avg_launch_us": attn_avg_ms * 1e3,
+            # the same launches replayed from a captured graph (no host latency)
+            "graph_avg_launch_us": m["attn_graph_us"],
         },
         "launch": "eager" if args.eager else "hip graph of one round",
         "eager_ms_per_step": m["eager_ms_step"],
