@@ -424,10 +424,11 @@ __global__ __launch_bounds__(kThreads) void markov_fold(Step st, int nblocks,
 // arithmetic is score_depth's, bit for bit the one-launch-a-depth form's.
 //
 // The launch is an ordinary one: the host admits the form only when every
-// block fits on the device at once (one 512-thread block a CU), so on a
-// device running nothing else all blocks start together. Other work on the
-// device can hold some blocks back; the others then wait, and a wait longer
-// than kWaitTicks abandons the pass (flag 2 from that depth on). A
+// block fits on the device at once (at rank 256 one 512-thread block a CU),
+// so on a device running nothing else all blocks start together; callers
+// run one resident pass at a time on a device. Other work on the device can
+// hold some blocks back; the others then wait, and a wait longer than
+// kWaitTicks abandons the pass (flag 2 from that depth on). A
 // cooperative launch would guarantee residency, but on this runtime it
 // waits on the host for the stream's earlier work and costs 15-20 us a
 // call on the device (measured: 112 against 93 us a pass).
