@@ -212,6 +212,13 @@ def test_markov_refusals_on_the_host():
               vocab=1000, rank=64, pick=A, flag=A)
     ws = asv.markov_workspace(1000)
     assert ws == 2 * 4 * 32 * 4      # two halves: a 4-byte record per chain and scan block
+    # the larger of the two forms' records: 4 bytes a 256-token block and
+    # chain, or 8 bytes a 512-token block and chain (resident)
+    for vocab in (1, 255, 256, 257, 512, 513, 131072, 600000):
+        launches = 2 * 32 * 4 * -(-vocab // 256)
+        resident = 2 * 32 * 8 * -(-vocab // 512)
+        assert asv.markov_workspace(vocab) == max(launches, resident), vocab
+    assert asv.markov_workspace(0) == 0 and asv.markov_workspace((1 << 30) + 1) == 0
 
     def call(workspace_bytes=ws, **kw):
         a = dict(ok, **kw)
@@ -230,6 +237,12 @@ def test_markov_refusals_on_the_host():
     assert call(base=None) == -1 and call(w1=A + 8) == -1
     assert call(workspace_bytes=ws - 1) == -4
     assert call(chains=[]) == 0                                   # nothing to do, no launch
+    a = dict(ok)
+    arr = (asv.MarkovChain * 2)(*[asv.MarkovChain(r, d) for r, d in a["chains"]])
+    for form in (-1, 3):                                          # an unknown form
+        assert asv.lib().asv_markov_pick_form(a["base"], a["rows"], a["row_stride"], arr, 2, a["prev0"],
+                                              a["w1"], a["w2c"], a["vocab"], a["rank"], a["pick"],
+                                              a["flag"], A, ws, form, 0) == -1
     assert asv.lib().asv_markov_pack_w2(A, 1000, 12, A * 3, 0) == -3
     assert asv.lib().asv_markov_pack_w2(A, 1000, 64, A + 64, 0) == -1   # overlapping
 
