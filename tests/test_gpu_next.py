@@ -286,3 +286,49 @@ def test_markov_ties_go_to_the_lowest_token(form):
     base[1, 2500] = 0x0000
     gp, gf = _check_markov(base, [(0, 2)], [1], w1, w2, form)
     assert gp.tolist() == [257, 0] and gf.tolist() == [0, 0]
+
+
+def test_markov_resident_graph_replays():
+    """The resident pass (its clearing launch and the pass itself) captured as
+    a HIP graph: every replay, with eager passes of other inputs and
+    synchronisations between the replays, gives the oracle's picks and flags
+    (the records are cleared by a kernel, not a memset, so each replay starts
+    clean)."""
+    rng = np.random.default_rng(19)
+    vocab, rank = 20000, 64
+    w1, w2 = _bf16(rng, (vocab, rank), 0.5), _bf16(rng, (vocab, rank), 0.5)
+    base = _bf16(rng, (16, vocab), 2.0)
+    chains, prev0 = [(0, 6), (6, 5), (11, 4)], [3, 19999, 1234]
+    W1 = _dev(w1.view(np.int16), torch.int16)
+    W2 = _dev(w2.view(np.int16), torch.int16)
+    W2c = torch.empty_like(W2)
+    asv.markov_pack_w2(W2, vocab, rank, W2c)
+    B = _dev(base.view(np.int16), torch.int16)
+    P0 = _dev(np.asarray(prev0, dtype=np.int32), torch.int32)
+    pick = torch.full((16,), -7, dtype=torch.int32, device="cuda")
+    flag = torch.full((16,), 9, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(asv.markov_workspace(vocab), dtype=torch.uint8, device="cuda")
+    rp, rf = _markov_ref(base, chains, prev0, w1, w2)
+    # other inputs for the eager passes between replays (the same workspace)
+    base2 = _bf16(rng, (16, vocab), 2.0)
+    B2 = _dev(base2.view(np.int16), torch.int16)
+    rp2, rf2 = _markov_ref(base2, [(2, 7)], prev0[:1], w1, w2)   # chain 0 of P0: token 3
+    pick2 = torch.full((16,), -7, dtype=torch.int32, device="cuda")
+    flag2 = torch.full((16,), 9, dtype=torch.uint8, device="cuda")
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        asv.markov_pick(B, 16, vocab, chains, P0, W1, W2c, vocab, rank, pick, flag, ws, form="resident")
+    for replay in range(4):
+        print(f"markov graph replay {replay}", flush=True)
+        pick.fill_(-7)
+        flag.fill_(9)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(pick.cpu().numpy(), rp), replay
+        assert np.array_equal(flag.cpu().numpy(), rf), replay
+        asv.markov_pick(B2, 16, vocab, [(2, 7)], P0, W1, W2c, vocab, rank, pick2, flag2, ws, form="resident")
+        torch.cuda.synchronize()
+        assert np.array_equal(pick2.cpu().numpy(), rp2), replay
+        assert np.array_equal(flag2.cpu().numpy(), rf2), replay
