@@ -244,12 +244,17 @@ def markov_leg(torch, asv, dev, seed, calls=20):
     fmas = depth * vocab * rank * len(chains)
     fma_peak = 256 * 64 * 2.4e9      # non-packed float32 FMA lanes of 256 CUs at 2.4 GHz
     return {"shape": "4 chains x depth 8, vocab 128,000, rank 256", "form": form,
+            # resident: W2 leaves HBM once a pass, and the pass is a chain of
+            # depths (record exchange, W1 rows, scoring); one launch a depth
+            # reads W2 at every depth and is bound by HBM
+            "bound": "alu" if form == "resident" else "hbm",
             "avg_call_us": us, "launches_per_call": n_launch, "bytes_per_call": nbytes,
             "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
             "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "fmas_per_call": fmas, "fma_frac": fmas / (us * 1e-6) / fma_peak,
             "launches_form_avg_call_us": us_launches,
-            "launches_form_bytes_per_call": launches_bytes}
+            "launches_form_bytes_per_call": launches_bytes,
+            "launches_form_frac": launches_bytes / (us_launches * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
 def measure_round(torch, asv, workloads, dev, config, steps, warmup, block=False, with_qk=False,
