@@ -147,6 +147,17 @@ def test_markov_pack_is_the_tiled_layout():
         assert np.array_equal(W2c.cpu().numpy().view(np.uint16).reshape(-1), want)
 
 
+@pytest.mark.parametrize("form", FORMS)
+def test_markov_bench_shape_parity(form):
+    """The pass the bench times: 4 chains x depth 8 (a hold pass of 32 rows)
+    at vocabulary 128,000 and rank 256, weights N(0, 0.3), logits N(0, 3)."""
+    rng = np.random.default_rng(20)
+    vocab, rank = 128000, 256
+    w1, w2 = _bf16(rng, (vocab, rank), 0.3), _bf16(rng, (vocab, rank), 0.3)
+    base = _bf16(rng, (32, vocab), 3.0)
+    _check_markov(base, [(0, 8), (8, 8), (16, 8), (24, 8)], [17, 4242, 90000, 127999], w1, w2, form)
+
+
 @pytest.mark.parametrize("form", FORMS + ["auto"])
 def test_markov_full_shape_parity(form):
     """vocabulary 128,000, rank 256: three chains of depths 3, 2, 1."""
