@@ -77,6 +77,31 @@ __device__ __forceinline__ void conv_row(const u32x4& b, const u32x4& c, const u
   store_bf16x8(yrow, y);
 }
 
+// Block order on the device: blocks are dealt to the 8 XCDs in turn (the
+// grid's linear index mod 8, each XCD with its own L2). With several row
+// pairs a tile the grid is (8, pairs, tiles8 / 2), tiles8 = the tile count
+// rounded up to 8: a block's XCD is blockIdx.x, and the row pairs of a
+// group g = blockIdx.x + 8 blockIdx.z = tile * 4 + channel group share it. A
+// row pair reads as history the two rows the pair before it reads as its
+// own, and on one XCD those rows leave HBM once (at 2,048 rows the launch
+// fetched 1.70x its input bytes when they did not, 1.09x now); blocks past
+// the last tile exit. With one pair (one-row windows) the grid is (tiles, 1,
+// 4): a tile's four channel groups land on one XCD, with its table records.
+template <bool ONE_PAIR>
+__device__ __forceinline__ void conv_block(int& tile, int& cgroup, int& pair) {
+  if (ONE_PAIR) {
+    tile = int(blockIdx.x);
+    cgroup = int(blockIdx.z);
+    pair = 0;
+  } else {
+    const int g = int(blockIdx.x) + 8 * int(blockIdx.z);
+    tile = g >> 2;
+    cgroup = g & 3;
+    pair = int(blockIdx.y);
+  }
+}
+
+template <bool ONE_PAIR>
 __global__ __launch_bounds__(kThreads) void conv_rows(TableView tv, int layer,
                                                       const uint16_t* __restrict__ X,
                                                       const uint16_t* __restrict__ W,
@@ -89,12 +114,15 @@ __global__ __launch_bounds__(kThreads) void conv_rows(TableView tv, int layer,
   const uint64_t* cstate = tv.conv_state;
   const int nstreams = tv.n_streams;
   asm volatile("" ::"s"(segs), "s"(cstate), "s"(nstreams), "s"(layer), "s"(X), "s"(W), "s"(Y));
-  const asv_tile T = cload(tv.tiles + blockIdx.x);
-  const int i0 = blockIdx.y * kRowsPerBlock;
+  int tile, cgroup, pair;
+  conv_block<ONE_PAIR>(tile, cgroup, pair);
+  if (!ONE_PAIR && tile >= tv.n_tiles) return;  // padding past the last tile
+  const asv_tile T = cload(tv.tiles + tile);
+  const int i0 = pair * kRowsPerBlock;
   if (i0 >= T.nrows) return;
   const bool two = i0 + 1 < T.nrows;
   const int p0 = T.pos0 + i0;           // window position of the block's first row (even)
-  const int c0 = (blockIdx.z * kThreads + threadIdx.x) * 8;
+  const int c0 = (cgroup * kThreads + threadIdx.x) * 8;
   const int64_t r0 = int64_t(T.row0) + i0;
 
   // Every load of the block is issued before any is waited for, so the
@@ -200,8 +228,13 @@ extern "C" int asv_shared_conv(const asv_table_info* info, const void* dev_blob,
   // one-row decode windows), so no block is launched only to exit
   const unsigned pairs = unsigned((info->max_tile_rows + asv::kRowsPerBlock - 1) / asv::kRowsPerBlock);
   if (pairs < 1 || pairs > unsigned(asv::kSub)) return ASV_E_ARG;
-  hipLaunchKernelGGL(asv::conv_rows, dim3(unsigned(info->n_tiles), pairs, asv::kChannelGroups),
-                     dim3(asv::kThreads),
-                     0, static_cast<hipStream_t>(stream), tv, int(layer), x, w, y);
+  static_assert(asv::kChannelGroups == 4, "the block order assumes four channel groups");
+  const unsigned tiles8 = (unsigned(info->n_tiles) + 7) / 8 * 8;
+  if (pairs == 1)
+    hipLaunchKernelGGL(asv::conv_rows<true>, dim3(unsigned(info->n_tiles), 1, asv::kChannelGroups),
+                       dim3(asv::kThreads), 0, static_cast<hipStream_t>(stream), tv, int(layer), x, w, y);
+  else
+    hipLaunchKernelGGL(asv::conv_rows<false>, dim3(8, pairs, tiles8 / 2), dim3(asv::kThreads), 0,
+                       static_cast<hipStream_t>(stream), tv, int(layer), x, w, y);
   return hipGetLastError() == hipSuccess ? ASV_OK : ASV_E_HIP;
 }
